@@ -1,0 +1,250 @@
+"""CPU oracle for the Float8 training linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library in
+``float8_mixed_precision_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, built with gcc, no fast-math);
+this module compiles it on demand and wraps it with numpy arrays.  Every
+function states the definition it follows; the sources are the Float8
+training section of "Torchtitan: A PyTorch Library for Parallelism Techniques
+explained" (section 3), the E4M3 encoding named on the "torchtitan" tutorial
+page (Part XI, item 9) and the bf16 mixed-precision policy on the same page
+(Part IV, Stage 5).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+
+
+def build(force: bool = False, src: str = SRC, out: str = _LIB_PATH) -> str:
+    """Compile oracle.c (or another copy of it) into a shared library."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    if force or not os.path.exists(out) or (
+            os.path.getmtime(out) < os.path.getmtime(src)):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", src, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def _ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class Oracle:
+    """numpy front end of one compiled copy of oracle.c."""
+
+    def __init__(self, lib_path: str):
+        lib = ctypes.CDLL(lib_path)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.orc_e4m3_value.restype = ctypes.c_double
+        lib.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.orc_e4m3_encode.restype = ctypes.c_uint8
+        lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.orc_e4m3_encode_array.argtypes = [P, P, i64]
+        lib.orc_bf16_to_f32.restype = ctypes.c_float
+        lib.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.orc_f32_to_bf16.restype = ctypes.c_uint16
+        lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+        lib.orc_f32_to_bf16_array.argtypes = [P, P, i64]
+        lib.orc_scale_from_amax.restype = ctypes.c_float
+        lib.orc_scale_from_amax.argtypes = [ctypes.c_float]
+        lib.orc_quantize.argtypes = [P, i64, i64, ctypes.c_int, P, P, P, P, P]
+        lib.orc_gemm_tn.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int,
+                                    i64, i64, i64, P, P]
+        lib.orc_gemm_tn_sampled.argtypes = [P, P, ctypes.c_int, P, P,
+                                            ctypes.c_int, i64, P, P, i64, P, P]
+        self.lib = lib
+        self.path = lib_path
+
+    # -------------------------------------------------------------- e4m3 --
+
+    def e4m3_value(self, code: int) -> float:
+        """Closed-form value of one E4M3 code (NaN for 0x7F / 0xFF)."""
+        return float(self.lib.orc_e4m3_value(int(code) & 0xFF))
+
+    def e4m3_values(self) -> np.ndarray:
+        """float64 values of all 256 codes, indexed by code."""
+        return np.array([self.lib.orc_e4m3_value(c) for c in range(256)],
+                        dtype=np.float64)
+
+    def e4m3_encode(self, y) -> np.ndarray:
+        """Saturating round-to-nearest-even E4M3 encode of fp32 values."""
+        y = _c(y, np.float32)
+        out = np.empty(y.shape, dtype=np.uint8)
+        self.lib.orc_e4m3_encode_array(_ptr(y), _ptr(out), y.size)
+        return out
+
+    # -------------------------------------------------------------- bf16 --
+
+    @staticmethod
+    def bf16_to_f32(h) -> np.ndarray:
+        """Exact widening of bf16 bit patterns (uint16) to fp32."""
+        h = _c(h, np.uint16)
+        return (h.astype(np.uint32) << 16).view(np.float32)
+
+    def f32_to_bf16(self, v) -> np.ndarray:
+        """Nearest-even rounding of fp32 values to bf16 bit patterns."""
+        v = _c(v, np.float32)
+        out = np.empty(v.shape, dtype=np.uint16)
+        self.lib.orc_f32_to_bf16_array(_ptr(v), _ptr(out), v.size)
+        return out
+
+    # ---------------------------------------------------------- quantize --
+
+    def scale_from_amax(self, a: float) -> np.float32:
+        """fp32 scale 448 / max(a, 1e-12), one IEEE division."""
+        return np.float32(self.lib.orc_scale_from_amax(float(np.float32(a))))
+
+    def quantize(self, x_bits, rowwise: bool = False):
+        """Quantize a bf16 matrix (uint16 bit patterns, shape [rows, cols]).
+
+        Returns (q [rows, cols] u8, qt [cols, rows] u8, scale, scale_t, amax):
+        tensorwise -> scale, scale_t of shape [1] (equal) and amax [1];
+        rowwise    -> scale [rows] (row scales, used by q), scale_t [cols]
+                      (column scales, used by qt) and amax [rows + cols].
+        """
+        x = _c(x_bits, np.uint16)
+        rows, cols = x.shape
+        q = np.empty((rows, cols), dtype=np.uint8)
+        qt = np.empty((cols, rows), dtype=np.uint8)
+        if rowwise:
+            s = np.empty(rows, np.float32)
+            st = np.empty(cols, np.float32)
+            am = np.empty(rows + cols, np.float32)
+        else:
+            s = np.empty(1, np.float32)
+            st = np.empty(1, np.float32)
+            am = np.empty(1, np.float32)
+        self.lib.orc_quantize(_ptr(x), rows, cols, int(bool(rowwise)), _ptr(q),
+                              _ptr(qt), _ptr(s), _ptr(st), _ptr(am))
+        return q, qt, s, st, am
+
+    # -------------------------------------------------------------- GEMM --
+
+    def gemm_tn(self, a, sa, b, sb, return_acc: bool = False):
+        """out[i, j] = bf16(fl32(fl32(acc * (1/sa_i)) * (1/sb_j))) with
+        acc = sum_t value(a[i, t]) * value(b[j, t]) in fp32, ascending t.
+
+        a: u8 [m, k], b: u8 [n, k]; sa: fp32 [1] or [m]; sb: fp32 [1] or
+        [n].  Returns bf16 bit patterns [m, n] (and the fp32 sums)."""
+        a = _c(a, np.uint8)
+        b = _c(b, np.uint8)
+        sa = _c(np.atleast_1d(sa), np.float32)
+        sb = _c(np.atleast_1d(sb), np.float32)
+        m, k = a.shape
+        n, k2 = b.shape
+        assert k == k2
+        assert sa.size in (1, m) and sb.size in (1, n)
+        out = np.empty((m, n), dtype=np.uint16)
+        acc = np.empty((m, n), dtype=np.float32) if return_acc else None
+        self.lib.orc_gemm_tn(_ptr(a), _ptr(sa), int(sa.size != 1), _ptr(b),
+                             _ptr(sb), int(sb.size != 1), m, n, k, _ptr(out),
+                             _ptr(acc))
+        return (out, acc) if return_acc else out
+
+    def gemm_tn_sampled(self, a, sa, b, sb, ii, jj, return_acc: bool = False):
+        """The same definition as gemm_tn, evaluated only at (ii[s], jj[s])."""
+        a = _c(a, np.uint8)
+        b = _c(b, np.uint8)
+        sa = _c(np.atleast_1d(sa), np.float32)
+        sb = _c(np.atleast_1d(sb), np.float32)
+        ii = _c(ii, np.int64)
+        jj = _c(jj, np.int64)
+        m, k = a.shape
+        n, k2 = b.shape
+        assert k == k2 and ii.shape == jj.shape
+        assert sa.size in (1, m) and sb.size in (1, n)
+        if ii.size:
+            assert ii.min() >= 0 and ii.max() < m
+            assert jj.min() >= 0 and jj.max() < n
+        out = np.empty(ii.shape, dtype=np.uint16)
+        acc = np.empty(ii.shape, dtype=np.float32) if return_acc else None
+        self.lib.orc_gemm_tn_sampled(_ptr(a), _ptr(sa), int(sa.size != 1),
+                                     _ptr(b), _ptr(sb), int(sb.size != 1), k,
+                                     _ptr(ii), _ptr(jj), ii.size, _ptr(out),
+                                     _ptr(acc))
+        return (out, acc) if return_acc else out
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from oracle.c (compiled on first use)."""
+    global _default
+    if _default is None:
+        _default = Oracle(build())
+    return _default
+
+
+def e4m3_value(code):
+    return default().e4m3_value(code)
+
+
+def e4m3_values():
+    return default().e4m3_values()
+
+
+def e4m3_encode(y):
+    return default().e4m3_encode(y)
+
+
+def bf16_to_f32(h):
+    return Oracle.bf16_to_f32(h)
+
+
+def f32_to_bf16(v):
+    return default().f32_to_bf16(v)
+
+
+def scale_from_amax(a):
+    return default().scale_from_amax(a)
+
+
+def quantize(x_bits, rowwise=False):
+    return default().quantize(x_bits, rowwise)
+
+
+def gemm_tn(a, sa, b, sb, return_acc=False):
+    return default().gemm_tn(a, sa, b, sb, return_acc)
+
+
+def gemm_tn_sampled(a, sa, b, sb, ii, jj, return_acc=False):
+    return default().gemm_tn_sampled(a, sa, b, sb, ii, jj, return_acc)
+
+
+# ------------------------------------------------------- parity metrics --
+
+def bf16_ulp_distance(g_bits, o_bits) -> np.ndarray:
+    """|ord(g) - ord(o)| on sign-magnitude-ordered bf16 patterns (+0 == -0)."""
+    def order(h):
+        h = np.asarray(h, dtype=np.uint16).astype(np.int64)
+        mag = h & 0x7FFF
+        return np.where(h & 0x8000, -mag, mag)
+    return np.abs(order(g_bits) - order(o_bits))
+
+
+def rel_frobenius(g_bits, o_bits) -> float:
+    """||G - O||_F / ||O||_F in float64 over the bf16 values of both."""
+    g = bf16_to_f32(g_bits).astype(np.float64)
+    o = bf16_to_f32(o_bits).astype(np.float64)
+    den = np.sqrt(np.sum(o * o))
+    num = np.sqrt(np.sum((g - o) ** 2))
+    return float(num / den) if den > 0 else float(num)

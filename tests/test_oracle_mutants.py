@@ -1,0 +1,63 @@
+"""Planted mistakes: each case copies oracle.c, plants one plausible mistake
+(on the CPU, in a temporary directory), builds it and requires that at least
+one pin fails on it.  This shows the pins are strong enough to catch a
+dropped term, a wrong sign, a wrong index or a wrong rounding in the oracle."""
+import os
+
+import pytest
+
+import oracle
+from tests import pins
+
+MUTANTS = {
+    # encode: ties go to the lower code instead of the even one
+    "tie_to_lower": ("else                code = (lo % 2 == 0) ? lo : hi;",
+                     "else                code = lo;"),
+    # encode: negative values that round to zero lose their sign
+    "sign_from_compare": ("uint8_t sign = signbit(y) ? 0x80 : 0x00;",
+                          "uint8_t sign = (y < 0) ? 0x80 : 0x00;"),
+    # encode: no saturation, overflow takes the NaN code
+    "no_saturation": ("if (m >= ORC_E4M3_MAX) return (uint8_t)(sign | 0x7E);",
+                      "if (m >= 464.0) return (uint8_t)(sign | 0x7F);"),
+    # decode: subnormal exponent off by one
+    "subnormal_exp": ("if (e == 0) mag = ldexp((double)f, -9);",
+                      "if (e == 0) mag = ldexp((double)f, -10);"),
+    # scale: reciprocal-then-multiply instead of one division
+    "scale_reciprocal": ("return (float)ORC_E4M3_MAX / d;",
+                         "return (float)ORC_E4M3_MAX * (1.0f / d);"),
+    # quantize: column copy uses the row scale
+    "qt_row_scale": ("qt[c * rows + r] = orc_e4m3_encode(orc_bf16_to_f32(x[r * cols + c]) * s);",
+                     "qt[c * rows + r] = orc_e4m3_encode(orc_bf16_to_f32(x[r * cols + c]) * scale[r]);"),
+    # amax: absolute value dropped
+    "amax_no_abs": ("float m = fabsf(v);", "float m = v;"),
+    # GEMM: wrong operand index (first term of B taken from A's row)
+    "gemm_operand": ("acc += val32[arow[t]] * val32[brow[t]];",
+                     "acc += val32[arow[t]] * val32[arow[t]];"),
+    # GEMM: one term dropped
+    "gemm_drop_term": ("for (int64_t t = 0; t < k; t++)\n        acc +=",
+                       "for (int64_t t = 1; t < k; t++)\n        acc +="),
+    # epilogue: B's reciprocal taken from A's scale
+    "epilogue_scale": ("float inv_b = 1.0f / sb;", "float inv_b = 1.0f / sa;"),
+    # epilogue: bf16 rounding truncates
+    "bf16_truncate": ("if (dd < du) return down;", "if (1) return down;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, "mutation site not found: %s" % name
+    path = os.path.join(str(tmp_path), "oracle_%s.c" % name)
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.build(force=True, src=path, out=os.path.join(str(tmp_path), "lib%s.so" % name))
+    mutant = oracle.Oracle(lib)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(mutant)
+        except AssertionError as e:
+            caught.append("%s: %s" % (check.__name__, e))
+            break
+    assert caught, "no pin caught mutant %s" % name
