@@ -1,0 +1,242 @@
+"""Benchmark: Float8 linear fwd+bwd on one MI355X.
+
+One step = the whole path for every linear of the workload: quantize X, W
+and dY (amax, scale, saturating E4M3 cast with the transposed copy), the
+forward GEMM and both backward GEMMs, all on device-resident synthetic
+inputs (seeded, Llama-3.1-shaped).  The default workload is the Llama-3.1-8B
+SwiGLU FFN (w1 and w3: X[8192x4096].W[14336x4096]^T, w2:
+X[8192x14336].W[4096x14336]^T), tensorwise scaling.
+
+Prints one JSON line: whole-step TFLOP/s (6*M*N*K per linear), the roofline
+of the dominant kernel (the fp8 GEMM, against the dense fp8 MFMA peak)
+measured with HIP events on the launch stream during the timed steps, the
+same for the quantize chain against HBM bandwidth, and the CPU oracle timed
+on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "float8_mixed_precision_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="ffn8b_tw")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the CPU oracle timing (e.g. under a profiler)")
+    p.add_argument("--cpu-rows", type=int, default=128,
+                   help="output rows per GEMM in the CPU oracle sample")
+    return p.parse_args()
+
+
+def gemm_source_hash() -> str:
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, valid
+    only while the GEMM source is the one the counters were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, rows_g: int, rows_q: int = 512):
+    """The oracle, as it stands, on a bounded sample of the same step:
+    quantize of the first rows_q rows of every input and rows_g output rows
+    of every GEMM, each scaled to its full size."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(0)
+
+    def codes(shape):
+        c = rng.integers(0, 256, shape, dtype=np.uint8)
+        c[(c & 0x7F) == 0x7F] = 0
+        return c
+
+    orc = oracle.default()
+    est = 0.0
+    flops_sampled = 0
+    t_wall = time.perf_counter()
+    for lin in wl.linears:
+        M, N, K = lin.M, lin.N, lin.K
+        for (r, c) in ((M, K), (N, K), (M, N)):
+            x = rng.integers(0, 1 << 15, (min(rows_q, r), c), dtype=np.uint16)
+            x[(x & 0x7F80) == 0x7F80] = 0
+            t = time.perf_counter()
+            orc.quantize(x, wl.rowwise)
+            est += (time.perf_counter() - t) * r / x.shape[0]
+        # (out rows, inner, other operand rows): fwd, grad_x, grad_w
+        for (m, k, n) in ((M, K, N), (M, N, K), (N, M, K)):
+            a = codes((min(rows_g, m), k))
+            b = codes((n, k))
+            s = np.ones(1, np.float32)
+            t = time.perf_counter()
+            orc.gemm_tn(a, s, b, s)
+            dt = time.perf_counter() - t
+            flops_sampled += 2 * a.shape[0] * n * k
+            est += dt * m / a.shape[0]
+    wall = time.perf_counter() - t_wall
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": wl.flops / est / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "oracle quantize of %d rows per input and %d output rows per GEMM "
+                      "(%.1f GFLOP, %.1f s), each scaled to the full step; estimated "
+                      "%.1f s per step" % (rows_q, rows_g, flops_sampled / 1e9, wall, est)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from float8_mixed_precision_amd import ops
+    from float8_mixed_precision_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating %s" % wl.name, file=sys.stderr, flush=True)
+    data = W.generate(wl)
+    steps = []
+    shared = {}
+    for lin, d in zip(wl.linears, data):
+        key = id(d["x"])
+        if key not in shared:
+            shared[key] = W.bits_to_torch(d["x"], dev)
+        steps.append(ops.LinearStep(shared[key], W.bits_to_torch(d["w"], dev),
+                                    W.bits_to_torch(d["dy"], dev), wl.rowwise))
+    del data
+    stream = torch.cuda.current_stream()
+
+    # per-op events: (kind, flops or bytes, start, end)
+    def run_step(record):
+        evs = []
+        for ls in steps:
+            M, N, K, rw = ls.M, ls.N, ls.K, ls.rowwise
+            ops_list = (
+                ("quantize", 6 * M * K, lambda: ops.fp8_linear_quantize(ls.x, rw, ls.qx, ls.ws)),
+                ("quantize", 6 * N * K, lambda: ops.fp8_linear_quantize(ls.w, rw, ls.qw, ls.ws)),
+                ("quantize", 6 * M * N, lambda: ops.fp8_linear_quantize(ls.dy, rw, ls.qdy, ls.ws)),
+                ("gemm", 2 * M * N * K, lambda: ops.fp8_linear_fwd(
+                    ls.qx.q, ls.qx.scale, ls.qw.q, ls.qw.scale, rw, ls.out)),
+                ("gemm", 2 * M * N * K, lambda: ops.fp8_linear_bwd(
+                    ls.qdy.q, ls.qdy.scale, None, None, ls.qw.qt, ls.qw.scale_t, None, None,
+                    M, N, K, rw, grad_x=ls.grad_x, want_w=False)),
+                ("gemm", 2 * M * N * K, lambda: ops.fp8_linear_bwd(
+                    None, None, ls.qdy.qt, ls.qdy.scale_t, None, None, ls.qx.qt, ls.qx.scale_t,
+                    M, N, K, rw, grad_w=ls.grad_w, want_x=False)),
+            )
+            for kind, work, fn in ops_list:
+                if record:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                    evs.append((kind, work, e0, e1))
+                else:
+                    fn()
+        return evs
+
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        run_step(False)
+    torch.cuda.synchronize()
+
+    print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    all_evs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        all_evs += run_step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    def agg(kind):
+        work = sum(w for k, w, _, _ in all_evs if k == kind)
+        ms = sum(a.elapsed_time(b) for k, _, a, b in all_evs if k == kind)
+        n = sum(1 for k, _, _, _ in all_evs if k == kind)
+        return work, ms, n
+
+    g_flops, g_ms, g_n = agg("gemm")
+    q_bytes, q_ms, q_n = agg("quantize")
+    gemm_tflops = g_flops / (g_ms * 1e-3) / 1e12
+    quant_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+    value = wl.flops * args.steps / elapsed / 1e12
+
+    traffic = measured_traffic()
+    result = {
+        "metric": "fp8 linear fwd+bwd TFLOP/s at Llama-3.1-8B FFN shape; % fp8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 in/out)",
+        "data": "synthetic (seeded numpy draws rounded to bf16; device-resident)",
+        "config": {"workload": wl.name, "description": wl.description,
+                   "scaling": "rowwise" if wl.rowwise else "tensorwise",
+                   "linears": [{"name": l.name, "M": l.M, "N": l.N, "K": l.K}
+                               for l in wl.linears],
+                   "flops_per_step": wl.flops},
+        "pct_fp8_peak_step": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "roofline": {
+            "kernel": "k_gemm_fp8_tn (fwd, grad_x, grad_w launches)",
+            "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": traffic,
+            "launches": g_n, "avg_launch_us": round(g_ms * 1e3 / g_n, 2),
+            "avg_flops_per_launch": g_flops // g_n,
+        },
+        "roofline_quantize": {
+            "kernel": "amax + finalize + cast_transpose chain per tensor",
+            "bound": "hbm", "achieved": round(quant_gbs, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(quant_gbs / PEAK_HBM_GBS, 4),
+            "bytes_per_element": 6, "calls": q_n, "avg_call_us": round(q_ms * 1e3 / q_n, 2),
+        },
+        "time_split_ms_per_step": {"gemm": round(g_ms / args.steps, 4),
+                                   "quantize": round(q_ms / args.steps, 4)},
+        "cpu_baseline": None,
+    }
+    del steps, shared
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

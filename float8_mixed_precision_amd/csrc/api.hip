@@ -1,0 +1,133 @@
+// C ABI of the Float8 linear library (declared in include/fp8_linear.h):
+// argument validation on the host, then asynchronous launches on the
+// caller's stream.  Nothing here allocates, synchronizes or keeps state.
+#include "fp8l_internal.h"
+
+namespace {
+
+bool bad_dim(int64_t d) { return d < 0 || (d % 16) != 0 || d > (int64_t)1 << 30; }
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Dimensions are capped at 2^30 so that every 32-bit index in the kernels
+// stays in range (addresses are formed in 64 bits), and a matrix at 2^40
+// elements so that grid sizes fit in 32 bits.
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+// C[m,n] = A[m,k] . B[n,k]^T: a pointer may be NULL only where its matrix
+// is empty; the scales are read whenever an output element is written.
+int check_gemm_operands(const void *a, const float *sa, const void *b,
+                        const float *sb, const void *c, int64_t m, int64_t n,
+                        int64_t k) {
+  if ((!a && m * k > 0) || (!b && n * k > 0) || (!c && m * n > 0)) return FP8L_EINVAL;
+  if ((!sa || !sb) && m * n > 0) return FP8L_EINVAL;
+  if (misaligned(a) || misaligned(b) || misaligned(c)) return FP8L_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(sa) & 3u) || (reinterpret_cast<uintptr_t>(sb) & 3u))
+    return FP8L_EALIGN;
+  return FP8L_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fp8_linear_workspace_bytes(int64_t rows, int64_t cols, int scaling) {
+  if (bad_dim(rows) || bad_dim(cols)) return 0;
+  if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return 0;
+  return fp8l::quantize_workspace_bytes(rows, cols, scaling);
+}
+
+int fp8_linear_quantize(const void *x, int64_t rows, int64_t cols, int scaling,
+                        void *q, void *qt, float *scale, float *scale_t,
+                        float *amax_out, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return FP8L_EINVAL;
+  if (bad_dim(rows) || bad_dim(cols) || rows * cols > kMaxElems) return FP8L_ESHAPE;
+  const bool empty = rows == 0 || cols == 0;
+  // scale vectors may be NULL only where they have no entries (rowwise, 0 rows
+  // or 0 columns); tensorwise scales always have one entry
+  const bool rw = scaling == FP8L_ROWWISE;
+  if ((!scale && (!rw || rows > 0)) || (!scale_t && (!rw || cols > 0))) return FP8L_EINVAL;
+  if (!empty && (!x || !q || !qt)) return FP8L_EINVAL;
+  const size_t need = fp8l::quantize_workspace_bytes(rows, cols, scaling);
+  if (need > 0 && !workspace) return FP8L_EINVAL;
+  if (workspace_bytes < need) return FP8L_EWORKSPACE;
+  if (misaligned(x) || misaligned(q) || misaligned(qt) || misaligned(workspace))
+    return FP8L_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(scale) & 3u) || (reinterpret_cast<uintptr_t>(scale_t) & 3u) ||
+      (reinterpret_cast<uintptr_t>(amax_out) & 3u))
+    return FP8L_EALIGN;
+  hipError_t e = fp8l::quantize_launch(x, rows, cols, scaling, q, qt, scale, scale_t,
+                                       amax_out, workspace,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
+int fp8_linear_fwd(const void *xq, const float *sx, const void *wq,
+                   const float *sw, int64_t M, int64_t N, int64_t K,
+                   int scaling, void *out, void *stream) {
+  if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return FP8L_EINVAL;
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8L_ESHAPE;
+  if (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems) return FP8L_ESHAPE;
+  int s = check_gemm_operands(xq, sx, wq, sw, out, M, N, K);
+  if (s != FP8L_OK) return s;
+  const int vec = scaling == FP8L_ROWWISE;
+  hipError_t e = fp8l::gemm_launch(static_cast<const uint8_t *>(xq), sx, vec,
+                                   static_cast<const uint8_t *>(wq), sw, vec, M, N, K,
+                                   static_cast<uint16_t *>(out),
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
+int fp8_linear_bwd(const void *dyq, const float *sdy, const void *dytq,
+                   const float *sdyt, const void *wtq, const float *swt,
+                   const void *xtq, const float *sxt, int64_t M, int64_t N,
+                   int64_t K, int scaling, void *grad_x, void *grad_w,
+                   void *stream) {
+  if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return FP8L_EINVAL;
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8L_ESHAPE;
+  if (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems) return FP8L_ESHAPE;
+  if (!grad_x && !grad_w) return FP8L_EINVAL;
+  int s;
+  if (grad_x && (s = check_gemm_operands(dyq, sdy, wtq, swt, grad_x, M, K, N)) != FP8L_OK)
+    return s;
+  if (grad_w && (s = check_gemm_operands(dytq, sdyt, xtq, sxt, grad_w, N, K, M)) != FP8L_OK)
+    return s;
+  const int vec = scaling == FP8L_ROWWISE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (grad_x)  // [M,K] = dYq[M,N] . WTq[K,N]^T
+    e = fp8l::gemm_launch(static_cast<const uint8_t *>(dyq), sdy, vec,
+                          static_cast<const uint8_t *>(wtq), swt, vec, M, K, N,
+                          static_cast<uint16_t *>(grad_x), st);
+  if (e == hipSuccess && grad_w)  // [N,K] = dYTq[N,M] . XTq[K,M]^T
+    e = fp8l::gemm_launch(static_cast<const uint8_t *>(dytq), sdyt, vec,
+                          static_cast<const uint8_t *>(xtq), sxt, vec, N, K, M,
+                          static_cast<uint16_t *>(grad_w), st);
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
+int fp8_linear_encode_e4m3(const float *in, uint8_t *out, int64_t n, void *stream) {
+  if (n < 0 || n > kMaxElems) return FP8L_ESHAPE;
+  if (n == 0) return FP8L_OK;
+  if (!in || !out) return FP8L_EINVAL;
+  if (misaligned(in) || misaligned(out)) return FP8L_EALIGN;
+  hipError_t e = fp8l::encode_launch(in, out, n, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
+const char *fp8_linear_status_string(int status) {
+  switch (status) {
+    case FP8L_OK: return "ok";
+    case FP8L_EINVAL: return "invalid argument (null pointer or unknown enum)";
+    case FP8L_ESHAPE: return "invalid shape (dimension < 0 or not a multiple of 16)";
+    case FP8L_EALIGN: return "misaligned pointer (tensors need 16-byte alignment)";
+    case FP8L_EWORKSPACE: return "workspace too small";
+    case FP8L_EHIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *fp8_linear_version(void) { return "fp8_linear 0.1 gfx950"; }
+
+}  // extern "C"

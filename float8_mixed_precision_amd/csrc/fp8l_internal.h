@@ -1,0 +1,60 @@
+// Internal declarations of the gfx950 Float8 linear library: device helpers
+// shared by the kernels and the host-side launchers called by the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp8_linear.h"
+
+namespace fp8l {
+
+// ------------------------------------------------------------ device math --
+
+// bf16 bit pattern -> fp32 (exact: bf16 is the upper half of an fp32).
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
+  return __uint_as_float(h16 << 16);
+}
+
+// Saturating round-to-nearest-even E4M3 ("fn") codes of four fp32 values,
+// packed little-endian into one dword (a in byte 0 ... d in byte 3).
+// Magnitudes >= 448 clamp to 448 before the hardware conversion (which
+// rounds to nearest even); NaN bypasses the clamp so it stays NaN.
+__device__ __forceinline__ float sat448(float v) {
+  float c = __builtin_amdgcn_fmed3f(v, -FP8L_E4M3_MAX, FP8L_E4M3_MAX);
+  return (v != v) ? v : c;
+}
+
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+  return (uint32_t)w;
+}
+
+// Scale from an amax given as |bf16| bits: s = 448 / max(a, 1e-12) as one
+// IEEE fp32 division (HIP's default fp32 divide is correctly rounded).  A
+// NaN amax compares false and yields NaN.
+__device__ __forceinline__ float scale_from_amax(float a) {
+  float d = (a < FP8L_AMAX_EPS) ? FP8L_AMAX_EPS : a;
+  return FP8L_E4M3_MAX / d;
+}
+
+// ---------------------------------------------------------- host launchers --
+
+// Quantize (amax partials -> scales -> cast + transpose), all enqueued on
+// `stream`.  Arguments were validated by the C ABI.
+size_t quantize_workspace_bytes(int64_t rows, int64_t cols, int scaling);
+hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
+                           int scaling, void *q, void *qt, float *scale,
+                           float *scale_t, float *amax_out, void *workspace,
+                           hipStream_t stream);
+hipError_t encode_launch(const float *in, uint8_t *out, int64_t n,
+                         hipStream_t stream);
+
+// C[M,N] (bf16) = (A[M,K] . B[N,K]^T) * (1/sa) * (1/sb); sa has M entries
+// when a_vec, else 1; sb has N entries when b_vec, else 1.
+hipError_t gemm_launch(const uint8_t *A, const float *sa, int a_vec,
+                       const uint8_t *B, const float *sb, int b_vec, int64_t M,
+                       int64_t N, int64_t K, uint16_t *C, hipStream_t stream);
+
+}  // namespace fp8l

@@ -1,0 +1,382 @@
+// Dynamic-scaling quantization of a bf16 matrix to E4M3 on gfx950:
+//   1. k_amax_partial  : one read pass; per-tile maxima of |x| (tensorwise)
+//                        or per-tile row / column maxima (rowwise)
+//   2. k_finalize_*    : reduce the partials, s = 448 / max(amax, 1e-12)
+//   3. k_cast_transpose: second read pass; writes q (row-major) directly and
+//                        qt (the transpose) through an LDS tile
+// The method is Float8 training of linear layers ("Torchtitan: A PyTorch
+// Library for Parallelism Techniques explained", section 3, "Float8
+// Training"); the 8-bit format is E4M3, named on the "torchtitan" tutorial
+// page, Part XI, item 9.  The scaling recipe (dynamic amax, per tensor or per
+// row / column) is the reading stated in include/fp8_linear.h.
+//
+// The amax is taken on |bf16| bit patterns with integer max: for
+// non-negative values the bit order is the value order, and NaN patterns
+// (exponent all ones, mantissa non-zero) sort above +inf, so a NaN anywhere
+// makes the amax NaN without a floating-point compare.
+#include "fp8l_internal.h"
+
+namespace fp8l {
+namespace {
+
+// amax tile: 64 rows x 256 columns per 256-thread workgroup.  Each thread owns
+// one 8-column chunk (16 bytes of bf16) and walks 8 of the tile's rows.
+constexpr int AM_TR = 64;
+constexpr int AM_TC = 256;
+constexpr int AM_THREADS = 256;
+
+// cast tile: 128 rows x 128 columns per 256-thread workgroup.
+constexpr int CT_T = 128;
+constexpr int CT_THREADS = 256;
+
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
+  uint32_t hi = max(a >> 16, b >> 16);
+  return lo | (hi << 16);
+}
+
+// max over the two u16 halves of a dword
+__device__ __forceinline__ uint32_t hmax16(uint32_t a) {
+  return max(a & 0xFFFFu, a >> 16);
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+// max over the 32 lanes of each half-wave
+__device__ __forceinline__ uint32_t half_wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+struct U4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 load16(const void *p) {
+  uint4 v = *reinterpret_cast<const uint4 *>(p);
+  return {v.x, v.y, v.z, v.w};
+}
+
+// ----------------------------------------------------------------- amax --
+//
+// Tensorwise: part[tile] = max |x| over the tile (u16 bits).
+// Rowwise:    rowpart[tile_c][r] = max over the tile's columns of row r,
+//             colpart[tile_r][c] = max over the tile's rows of column c.
+template <bool ROWWISE>
+__global__ __launch_bounds__(AM_THREADS) void k_amax_partial(
+    const uint16_t *__restrict__ x, int rows, int cols, int tiles_c,
+    uint16_t *__restrict__ part, uint16_t *__restrict__ rowpart,
+    uint16_t *__restrict__ colpart) {
+  const int tid = threadIdx.x;
+  const int tile_c = blockIdx.x % tiles_c;
+  const int tile_r = blockIdx.x / tiles_c;
+  const int cx = tid & 31;        // 8-column chunk within the tile
+  const int ry = tid >> 5;        // 0..7, row phase
+  const int r0 = tile_r * AM_TR;
+  const int c = tile_c * AM_TC + cx * 8;
+  const bool col_ok = c < cols;
+
+  uint32_t acc = 0;               // tensorwise: packed max of |x| pairs
+  uint32_t cm[4] = {0, 0, 0, 0};  // rowwise: column maxima, 2 per dword
+#pragma unroll
+  for (int i = 0; i < AM_TR / 8; ++i) {
+    const int r = r0 + ry + 8 * i;
+    U4 v = {0, 0, 0, 0};
+    if (col_ok && r < rows) v = load16(x + (size_t)r * cols + c);
+    v.x &= 0x7FFF7FFFu;
+    v.y &= 0x7FFF7FFFu;
+    v.z &= 0x7FFF7FFFu;
+    v.w &= 0x7FFF7FFFu;
+    if (!ROWWISE) {
+      acc = max_u16x2(acc, max_u16x2(max_u16x2(v.x, v.y), max_u16x2(v.z, v.w)));
+    } else {
+      cm[0] = max_u16x2(cm[0], v.x);
+      cm[1] = max_u16x2(cm[1], v.y);
+      cm[2] = max_u16x2(cm[2], v.z);
+      cm[3] = max_u16x2(cm[3], v.w);
+      uint32_t rm = hmax16(max_u16x2(max_u16x2(v.x, v.y), max_u16x2(v.z, v.w)));
+      rm = half_wave_max(rm);      // the 32 lanes of a half-wave share row r
+      if (cx == 0 && r < rows) rowpart[(size_t)tile_c * rows + r] = (uint16_t)rm;
+    }
+  }
+
+  if (!ROWWISE) {
+    __shared__ uint32_t red[AM_THREADS / 64];
+    uint32_t m = wave_max(hmax16(acc));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t t = red[0];
+#pragma unroll
+      for (int w = 1; w < AM_THREADS / 64; ++w) t = max(t, red[w]);
+      part[blockIdx.x] = (uint16_t)t;
+    }
+  } else {
+    // reduce the column maxima over the 8 row phases through LDS
+    __shared__ uint32_t cred[8][AM_TC / 2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cred[ry][cx * 4 + j] = cm[j];
+    __syncthreads();
+    if (tid < AM_TC / 2) {
+      uint32_t t = cred[0][tid];
+#pragma unroll
+      for (int p = 1; p < 8; ++p) t = max_u16x2(t, cred[p][tid]);
+      const int cc = tile_c * AM_TC + tid * 2;
+      if (cc < cols) {
+        uint16_t *dst = colpart + (size_t)tile_r * cols + cc;
+        dst[0] = (uint16_t)(t & 0xFFFFu);
+        dst[1] = (uint16_t)(t >> 16);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- finalize --
+
+__global__ __launch_bounds__(1024) void k_finalize_tensorwise(
+    const uint16_t *__restrict__ part, int nparts, float *scale,
+    float *scale_t, float *amax_out) {
+  __shared__ uint32_t red[1024 / 64];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, (uint32_t)part[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t = max(t, red[w]);
+    const float a = bf16_to_f32(t);
+    const float s = scale_from_amax(a);
+    scale[0] = s;
+    scale_t[0] = s;
+    if (amax_out) amax_out[0] = a;
+  }
+}
+
+// one thread per output: rows first (max over tiles_c partials), then columns
+__global__ __launch_bounds__(256) void k_finalize_rowwise(
+    const uint16_t *__restrict__ rowpart, const uint16_t *__restrict__ colpart,
+    int rows, int cols, int tiles_c, int tiles_r, float *scale, float *scale_t,
+    float *amax_out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < rows) {
+    uint32_t m = 0;
+    for (int t = 0; t < tiles_c; ++t) m = max(m, (uint32_t)rowpart[(size_t)t * rows + i]);
+    const float a = bf16_to_f32(m);
+    scale[i] = scale_from_amax(a);
+    if (amax_out) amax_out[i] = a;
+  } else if (i < rows + cols) {
+    const int c = i - rows;
+    uint32_t m = 0;
+    for (int t = 0; t < tiles_r; ++t) m = max(m, (uint32_t)colpart[(size_t)t * cols + c]);
+    const float a = bf16_to_f32(m);
+    scale_t[c] = scale_from_amax(a);
+    if (amax_out) amax_out[rows + c] = a;
+  }
+}
+
+// -------------------------------------------------------- cast+transpose --
+//
+// Tile of 128 rows x 128 columns.  Thread (c8, rg): c8 = tid % 16 selects an
+// 8-column chunk, rg = tid / 16 a group of 4 consecutive rows; two passes
+// cover rows rg*4 + {0..3} and 64 + rg*4 + {0..3}.
+//
+// Phase A: 16-byte coalesced loads of bf16 (a wave reads 4 rows x 256 B per
+// instruction), scale, convert, 8-byte stores of q (4 rows x 128 B per
+// wave).  The 4 x 8 block of qt codes is transposed in registers into eight
+// dwords (4 consecutive rows of one column each) and written to the LDS tile
+// lds[col][row] (128 B per column).  The 16-byte row chunk of a column is
+// XOR-swizzled with the column's chunk index (col / 8) so that the 16 column
+// chunks of a wave spread over the banks.
+//
+// Phase B: each thread reads 16-byte chunks (16 rows of one column) from LDS
+// and stores them to qt: eight threads write one 128-byte qt row segment.
+template <bool ROWWISE>
+__global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
+    const uint16_t *__restrict__ x, int rows, int cols, int tiles_c,
+    const float *__restrict__ scale, const float *__restrict__ scale_t,
+    uint8_t *__restrict__ q, uint8_t *__restrict__ qt) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[CT_T * CT_T];
+  const int tid = threadIdx.x;
+  const int tile_c = blockIdx.x % tiles_c;
+  const int tile_r = blockIdx.x / tiles_c;
+  const int r0 = tile_r * CT_T;
+  const int c0 = tile_c * CT_T;
+  const int c8 = tid & 15;
+  const int rg = tid >> 4;
+  const int c = c0 + c8 * 8;
+  const bool col_ok = c < cols;
+
+  float sc[8];                    // column scales (rowwise) of the 8 columns
+  float s_t = 0.f;                // tensor scale
+  if (ROWWISE) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sc[j] = col_ok ? scale_t[c + j] : 0.f;
+  } else {
+    s_t = scale[0];
+  }
+
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rl = pass * 64 + rg * 4;   // local row of the 4-row group
+    const int r = r0 + rl;
+    // rows is a multiple of 16, so the 4 rows are all in or all out
+    const bool ok = col_ok && r < rows;
+    uint32_t lo[4], hi[4];               // qt codes: cols 0-3 / 4-7 of each row
+    if (ok) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const U4 v = load16(x + (size_t)(r + j) * cols + c);
+        float f[8];
+        f[0] = bf16_to_f32(v.x & 0xFFFFu); f[1] = bf16_to_f32(v.x >> 16);
+        f[2] = bf16_to_f32(v.y & 0xFFFFu); f[3] = bf16_to_f32(v.y >> 16);
+        f[4] = bf16_to_f32(v.z & 0xFFFFu); f[5] = bf16_to_f32(v.z >> 16);
+        f[6] = bf16_to_f32(v.w & 0xFFFFu); f[7] = bf16_to_f32(v.w >> 16);
+        const float s = ROWWISE ? scale[r + j] : s_t;
+        const uint32_t q0 = e4m3x4(f[0] * s, f[1] * s, f[2] * s, f[3] * s);
+        const uint32_t q1 = e4m3x4(f[4] * s, f[5] * s, f[6] * s, f[7] * s);
+        *reinterpret_cast<uint2 *>(q + (size_t)(r + j) * cols + c) = make_uint2(q0, q1);
+        if (ROWWISE) {
+          lo[j] = e4m3x4(f[0] * sc[0], f[1] * sc[1], f[2] * sc[2], f[3] * sc[3]);
+          hi[j] = e4m3x4(f[4] * sc[4], f[5] * sc[5], f[6] * sc[6], f[7] * sc[7]);
+        } else {
+          lo[j] = q0;
+          hi[j] = q1;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lo[j] = hi[j] = 0;
+    }
+    // 4x4 byte transposes: column k of the block = byte k of each row dword
+    uint32_t t[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int sh = 8 * k;
+      t[k] = ((lo[0] >> sh) & 0xFFu) | (((lo[1] >> sh) & 0xFFu) << 8) |
+             (((lo[2] >> sh) & 0xFFu) << 16) | (((lo[3] >> sh) & 0xFFu) << 24);
+      t[4 + k] = ((hi[0] >> sh) & 0xFFu) | (((hi[1] >> sh) & 0xFFu) << 8) |
+                 (((hi[2] >> sh) & 0xFFu) << 16) | (((hi[3] >> sh) & 0xFFu) << 24);
+    }
+    const int chunk = rl >> 4;                // 16-row chunk of the column
+    const int pchunk = chunk ^ (c8 & 7);
+    const int inner = rl & 15;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int col = c8 * 8 + k;
+      *reinterpret_cast<uint32_t *>(lds + col * CT_T + pchunk * 16 + inner) = t[k];
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int p = 0; p < (CT_T * CT_T / 16) / CT_THREADS; ++p) {
+    const int id = tid + p * CT_THREADS;
+    const int col = id >> 3;
+    const int rc = id & 7;
+    const int gc = c0 + col;
+    const int gr = r0 + rc * 16;
+    if (gc < cols && gr < rows) {
+      const int pc = rc ^ ((col >> 3) & 7);
+      const uint4 v = *reinterpret_cast<const uint4 *>(lds + col * CT_T + pc * 16);
+      *reinterpret_cast<uint4 *>(qt + (size_t)gc * rows + gr) = v;
+    }
+  }
+}
+
+// --------------------------------------------------------------- encode --
+
+__global__ __launch_bounds__(256) void k_encode(const float *__restrict__ in,
+                                                uint8_t *__restrict__ out,
+                                                int64_t n) {
+  const int64_t n4 = n / 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4 v = reinterpret_cast<const float4 *>(in)[i];
+    reinterpret_cast<uint32_t *>(out)[i] = e4m3x4(v.x, v.y, v.z, v.w);
+  }
+  // tail (n not a multiple of 4)
+  const int64_t t = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n && t < n4 * 4 + 4) out[t] = (uint8_t)(e4m3x4(in[t], 0.f, 0.f, 0.f) & 0xFFu);
+}
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct AmaxGeom {
+  int64_t tiles_r, tiles_c;
+};
+
+AmaxGeom amax_geom(int64_t rows, int64_t cols) {
+  return {cdiv(rows, AM_TR), cdiv(cols, AM_TC)};
+}
+
+}  // namespace
+
+size_t quantize_workspace_bytes(int64_t rows, int64_t cols, int scaling) {
+  const AmaxGeom g = amax_geom(rows, cols);
+  size_t bytes;
+  if (scaling == FP8L_TENSORWISE)
+    bytes = (size_t)(g.tiles_r * g.tiles_c) * sizeof(uint16_t);
+  else
+    bytes = (size_t)(g.tiles_c * rows + g.tiles_r * cols) * sizeof(uint16_t) + 256;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
+                           int scaling, void *q, void *qt, float *scale,
+                           float *scale_t, float *amax_out, void *workspace,
+                           hipStream_t stream) {
+  const AmaxGeom g = amax_geom(rows, cols);
+  const int64_t ntiles = g.tiles_r * g.tiles_c;
+  const uint16_t *xb = static_cast<const uint16_t *>(x);
+  uint16_t *ws = static_cast<uint16_t *>(workspace);
+  const int R = (int)rows, C = (int)cols;
+  if (scaling == FP8L_TENSORWISE) {
+    if (ntiles > 0)
+      hipLaunchKernelGGL(k_amax_partial<false>, dim3((unsigned)ntiles), dim3(AM_THREADS), 0,
+                         stream, xb, R, C, (int)g.tiles_c, ws, nullptr, nullptr);
+    hipLaunchKernelGGL(k_finalize_tensorwise, dim3(1), dim3(1024), 0, stream, ws,
+                       (int)ntiles, scale, scale_t, amax_out);
+  } else {
+    uint16_t *rowpart = ws;
+    // column partials start on a 256-byte boundary after the row partials
+    size_t off = ((size_t)(g.tiles_c * rows) * sizeof(uint16_t) + 255) & ~(size_t)255;
+    uint16_t *colpart = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(workspace) + off);
+    if (ntiles > 0)
+      hipLaunchKernelGGL(k_amax_partial<true>, dim3((unsigned)ntiles), dim3(AM_THREADS), 0,
+                         stream, xb, R, C, (int)g.tiles_c, nullptr, rowpart, colpart);
+    if (rows + cols > 0)
+      hipLaunchKernelGGL(k_finalize_rowwise, dim3((unsigned)cdiv(rows + cols, 256)), dim3(256),
+                         0, stream, rowpart, colpart, R, C, (int)g.tiles_c, (int)g.tiles_r,
+                         scale, scale_t, amax_out);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ct_r = cdiv(rows, CT_T), ct_c = cdiv(cols, CT_T);
+  if (ct_r * ct_c > 0) {
+    if (scaling == FP8L_TENSORWISE)
+      hipLaunchKernelGGL(k_cast_transpose<false>, dim3((unsigned)(ct_r * ct_c)),
+                         dim3(CT_THREADS), 0, stream, xb, R, C, (int)ct_c, scale, scale_t,
+                         static_cast<uint8_t *>(q), static_cast<uint8_t *>(qt));
+    else
+      hipLaunchKernelGGL(k_cast_transpose<true>, dim3((unsigned)(ct_r * ct_c)),
+                         dim3(CT_THREADS), 0, stream, xb, R, C, (int)ct_c, scale, scale_t,
+                         static_cast<uint8_t *>(q), static_cast<uint8_t *>(qt));
+  }
+  return hipGetLastError();
+}
+
+hipError_t encode_launch(const float *in, uint8_t *out, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = cdiv(n / 4 + 1, 256);
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_encode, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace fp8l

@@ -1,0 +1,225 @@
+"""ctypes binding of the C ABI in include/fp8_linear.h.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library ``_lib/libfp8linear.so``.  torch supplies device memory
+(``torch.empty``) and the current stream; nothing here computes on tensor
+data, and there is no fallback: if the library is missing, loading raises.
+
+Names follow the C entry points.  Tensors are passed as ``data_ptr()``; the
+caller's tensors must be contiguous CUDA (HIP) tensors of the documented
+dtypes (bf16 for x / outputs, uint8 for the fp8 codes, float32 for scales).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_lib", "libfp8linear.so")
+
+FP8L_OK, FP8L_EINVAL, FP8L_ESHAPE, FP8L_EALIGN, FP8L_EWORKSPACE, FP8L_EHIP = range(6)
+FP8L_TENSORWISE, FP8L_ROWWISE = 0, 1
+EXPORTS = ("fp8_linear_workspace_bytes", "fp8_linear_quantize", "fp8_linear_fwd",
+           "fp8_linear_bwd", "fp8_linear_encode_e4m3", "fp8_linear_status_string",
+           "fp8_linear_version")
+
+
+class Fp8LinearError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, status_string(status), status))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("fp8 linear HIP library not built: %s is missing "
+                           "(run __graft_entry__.build())" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.fp8_linear_workspace_bytes.restype = ctypes.c_size_t
+    L.fp8_linear_workspace_bytes.argtypes = [i64, i64, I]
+    L.fp8_linear_quantize.restype = I
+    L.fp8_linear_quantize.argtypes = [P, i64, i64, I, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.fp8_linear_fwd.restype = I
+    L.fp8_linear_fwd.argtypes = [P, P, P, P, i64, i64, i64, I, P, P]
+    L.fp8_linear_bwd.restype = I
+    L.fp8_linear_bwd.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, I, P, P, P]
+    L.fp8_linear_encode_e4m3.restype = I
+    L.fp8_linear_encode_e4m3.argtypes = [P, P, i64, P]
+    L.fp8_linear_status_string.restype = ctypes.c_char_p
+    L.fp8_linear_status_string.argtypes = [I]
+    L.fp8_linear_version.restype = ctypes.c_char_p
+    L.fp8_linear_version.argtypes = []
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().fp8_linear_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != FP8L_OK:
+        raise Fp8LinearError(status, where)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _scaling(rowwise: bool) -> int:
+    return FP8L_ROWWISE if rowwise else FP8L_TENSORWISE
+
+
+# ----------------------------------------------------------- entry points --
+
+def fp8_linear_workspace_bytes(rows: int, cols: int, rowwise: bool = False) -> int:
+    return int(lib().fp8_linear_workspace_bytes(rows, cols, _scaling(rowwise)))
+
+
+class Quantized:
+    """Outputs of fp8_linear_quantize for one bf16 matrix x [rows, cols]."""
+
+    __slots__ = ("q", "qt", "scale", "scale_t", "amax")
+
+    def __init__(self, q, qt, scale, scale_t, amax):
+        self.q, self.qt, self.scale, self.scale_t, self.amax = q, qt, scale, scale_t, amax
+
+
+def alloc_quantized(rows: int, cols: int, rowwise: bool, device) -> Quantized:
+    ns, nst, na = (rows, cols, rows + cols) if rowwise else (1, 1, 1)
+    return Quantized(torch.empty((rows, cols), dtype=torch.uint8, device=device),
+                     torch.empty((cols, rows), dtype=torch.uint8, device=device),
+                     torch.empty(ns, dtype=torch.float32, device=device),
+                     torch.empty(nst, dtype=torch.float32, device=device),
+                     torch.empty(na, dtype=torch.float32, device=device))
+
+
+def alloc_workspace(rows: int, cols: int, rowwise: bool, device) -> torch.Tensor:
+    return torch.empty(max(fp8_linear_workspace_bytes(rows, cols, rowwise), 256),
+                       dtype=torch.uint8, device=device)
+
+
+def fp8_linear_quantize(x: torch.Tensor, rowwise: bool = False,
+                        out: Optional[Quantized] = None,
+                        workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> Quantized:
+    """Quantize bf16 x [rows, cols] -> (q, qt, scale, scale_t, amax)."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
+    rows, cols = x.shape
+    if out is None:
+        out = alloc_quantized(rows, cols, rowwise, x.device)
+    if workspace is None:
+        workspace = alloc_workspace(rows, cols, rowwise, x.device)
+    _check(lib().fp8_linear_quantize(
+        _p(x), rows, cols, _scaling(rowwise), _p(out.q), _p(out.qt), _p(out.scale),
+        _p(out.scale_t), _p(out.amax), _p(workspace), workspace.numel(), _stream(stream)),
+        "fp8_linear_quantize")
+    return out
+
+
+def fp8_linear_fwd(xq: torch.Tensor, sx: torch.Tensor, wq: torch.Tensor,
+                   sw: torch.Tensor, rowwise: bool = False,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out [M, N] bf16 = (xq [M, K] . wq [N, K]^T) / (sx * sw)."""
+    M, K = xq.shape
+    N = wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _check(lib().fp8_linear_fwd(_p(xq), _p(sx), _p(wq), _p(sw), M, N, K,
+                                _scaling(rowwise), _p(out), _stream(stream)),
+           "fp8_linear_fwd")
+    return out
+
+
+def fp8_linear_bwd(dyq, sdy, dytq, sdyt, wtq, swt, xtq, sxt, M: int, N: int, K: int,
+                   rowwise: bool = False, grad_x: Optional[torch.Tensor] = None,
+                   grad_w: Optional[torch.Tensor] = None, want_x: bool = True,
+                   want_w: bool = True, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """grad_x [M, K] = dY . W and grad_w [N, K] = dY^T . X from the fp8 copies."""
+    dev = (dyq if dyq is not None else dytq).device
+    if want_x and grad_x is None:
+        grad_x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if want_w and grad_w is None:
+        grad_w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    _check(lib().fp8_linear_bwd(_p(dyq), _p(sdy), _p(dytq), _p(sdyt), _p(wtq), _p(swt),
+                                _p(xtq), _p(sxt), M, N, K, _scaling(rowwise),
+                                _p(grad_x if want_x else None),
+                                _p(grad_w if want_w else None), _stream(stream)),
+           "fp8_linear_bwd")
+    return grad_x, grad_w
+
+
+def fp8_linear_encode_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """Device E4M3 saturating RNE codes of fp32 values."""
+    assert x.dtype == torch.float32 and x.is_contiguous()
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib().fp8_linear_encode_e4m3(_p(x), _p(out), x.numel(), _stream(stream)),
+           "fp8_linear_encode_e4m3")
+    return out
+
+
+def fp8_linear_version() -> str:
+    return lib().fp8_linear_version().decode()
+
+
+# ------------------------------------------------------------ one linear --
+
+class LinearStep:
+    """One Float8 linear fwd+bwd on preallocated device buffers.
+
+    Holds the bf16 inputs X [M, K], W [N, K], dY [M, N] and every output; a
+    call to ``run()`` enqueues quantize(X), quantize(W), quantize(dY), the
+    forward GEMM and both backward GEMMs on the current stream.
+    """
+
+    def __init__(self, x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor,
+                 rowwise: bool = False):
+        self.x, self.w, self.dy, self.rowwise = x, w, dy, rowwise
+        self.M, self.K = x.shape
+        self.N = w.shape[0]
+        dev = x.device
+        self.qx = alloc_quantized(self.M, self.K, rowwise, dev)
+        self.qw = alloc_quantized(self.N, self.K, rowwise, dev)
+        self.qdy = alloc_quantized(self.M, self.N, rowwise, dev)
+        ws = max(fp8_linear_workspace_bytes(self.M, self.K, rowwise),
+                 fp8_linear_workspace_bytes(self.N, self.K, rowwise),
+                 fp8_linear_workspace_bytes(self.M, self.N, rowwise), 256)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.out = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
+        self.grad_x = torch.empty((self.M, self.K), dtype=torch.bfloat16, device=dev)
+        self.grad_w = torch.empty((self.N, self.K), dtype=torch.bfloat16, device=dev)
+
+    def quantize(self, stream=None):
+        fp8_linear_quantize(self.x, self.rowwise, self.qx, self.ws, stream)
+        fp8_linear_quantize(self.w, self.rowwise, self.qw, self.ws, stream)
+        fp8_linear_quantize(self.dy, self.rowwise, self.qdy, self.ws, stream)
+
+    def gemms(self, stream=None):
+        fp8_linear_fwd(self.qx.q, self.qx.scale, self.qw.q, self.qw.scale, self.rowwise,
+                       self.out, stream)
+        fp8_linear_bwd(self.qdy.q, self.qdy.scale, self.qdy.qt, self.qdy.scale_t,
+                       self.qw.qt, self.qw.scale_t, self.qx.qt, self.qx.scale_t,
+                       self.M, self.N, self.K, self.rowwise, self.grad_x, self.grad_w,
+                       stream=stream)
+
+    def run(self, stream=None):
+        self.quantize(stream)
+        self.gemms(stream)

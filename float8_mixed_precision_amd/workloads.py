@@ -128,19 +128,31 @@ def tensor(seed: int, linear: int, t: int, shape, d: Dist) -> np.ndarray:
     return to_bf16_bits(_draw(rng, tuple(shape), d, rng_cols))
 
 
+def generate_linear(w: Workload, li: int) -> Dict[str, np.ndarray]:
+    """bf16 bit patterns {x, w, dy} of linear ``li`` of a workload."""
+    l = w.linears[li]
+    if l.x_from:
+        src = [k for k, o in enumerate(w.linears) if o.name == l.x_from][0]
+        x = tensor(w.seed, src, 0, (l.M, l.K), w.linears[src].x)
+    else:
+        x = tensor(w.seed, li, 0, (l.M, l.K), l.x)
+    return {"x": x,
+            "w": tensor(w.seed, li, 1, (l.N, l.K), l.w),
+            "dy": tensor(w.seed, li, 2, (l.M, l.N), l.dy)}
+
+
 def generate(w: Workload) -> List[Dict[str, np.ndarray]]:
-    """bf16 bit patterns for every linear of a workload: [{x, w, dy}, ...]."""
+    """bf16 bit patterns for every linear of a workload: [{x, w, dy}, ...].
+    A linear whose X comes from an earlier one shares that array."""
     out: List[Dict[str, np.ndarray]] = []
-    by_name: Dict[str, Dict[str, np.ndarray]] = {}
     for li, l in enumerate(w.linears):
         if l.x_from:
-            x = by_name[l.x_from]["x"]
+            src = [k for k, o in enumerate(w.linears) if o.name == l.x_from][0]
+            d = {"x": out[src]["x"],
+                 "w": tensor(w.seed, li, 1, (l.N, l.K), l.w),
+                 "dy": tensor(w.seed, li, 2, (l.M, l.N), l.dy)}
         else:
-            x = tensor(w.seed, li, 0, (l.M, l.K), l.x)
-        d = {"x": x,
-             "w": tensor(w.seed, li, 1, (l.N, l.K), l.w),
-             "dy": tensor(w.seed, li, 2, (l.M, l.N), l.dy)}
-        by_name[l.name] = d
+            d = generate_linear(w, li)
         out.append(d)
     return out
 

@@ -1,0 +1,166 @@
+/*
+ * fp8_linear.h -- C ABI of the MI355X (gfx950) Float8 training linear layer.
+ *
+ * The operation is Float8 training of a linear layer inside a bf16
+ * mixed-precision step: the layer's large GEMMs run with 8-bit operands
+ * ("Torchtitan: A PyTorch Library for Parallelism Techniques explained",
+ * section 3, "Float8 Training"; the forum index "torchtitan", topic
+ * "Enabling Float8 All-Gather in FSDP2": fp8 is used because it speeds up
+ * large GEMMs).  The 8-bit format is E4M3 from the FP8 formats paper named on
+ * the "torchtitan" tutorial page, Part XI, item 9; inputs and outputs are
+ * bf16 as in the tutorial page's mixed-precision policy (Part IV, Stage 5).
+ *
+ * One linear with X [M,K] (tokens x in-features), W [N,K] (out x in) and the
+ * output gradient dY [M,N] runs as:
+ *   quantize(X), quantize(W), quantize(dY)          -> fp8 copies + scales
+ *   fwd:  out    [M,N] = X  . W^T                   (Xq,   Wq)
+ *   bwd:  grad_X [M,K] = dY . W                     (dYq,  WTq)
+ *         grad_W [N,K] = dY^T . X                   (dYTq, XTq)
+ * Every GEMM reads two operands stored contiguous along the contraction
+ * index; quantize writes the transposed copy that makes this true.
+ *
+ * Conventions shared by every entry point
+ *  - All matrices are row-major and dense (leading dimension = #columns).
+ *  - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA memory),
+ *    16-byte aligned.  The caller owns every buffer; the library keeps no
+ *    state between calls, allocates nothing and never synchronizes.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously on it; results are ready when the stream reaches them.
+ *    Calls on different streams may run concurrently if their buffers do not
+ *    overlap.
+ *  - Dimensions must be >= 0 and multiples of 16 (FP8L_ESHAPE otherwise).
+ *    A zero dimension is an empty matrix: the call is valid and writes only
+ *    what its definition gives (scales of the empty set, zero outputs).
+ *  - Argument errors are detected on the host before anything is enqueued
+ *    and returned as a status code; nothing is written in that case.  A
+ *    failed launch returns FP8L_EHIP.  Non-finite input values are not
+ *    errors: they propagate into amax (NaN if any NaN, else inf if any inf)
+ *    so the caller can test it; the fp8 bytes are then unspecified.
+ */
+#ifndef FP8_LINEAR_H
+#define FP8_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define FP8L_API __attribute__((visibility("default")))
+#else
+#define FP8L_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (return value of every int-returning entry point). */
+#define FP8L_OK          0
+#define FP8L_EINVAL      1   /* null required pointer or unknown enum value */
+#define FP8L_ESHAPE      2   /* dimension < 0 or not a multiple of 16       */
+#define FP8L_EALIGN      3   /* a tensor pointer is not 16-byte aligned     */
+#define FP8L_EWORKSPACE  4   /* workspace smaller than required             */
+#define FP8L_EHIP        5   /* a HIP launch or runtime call failed         */
+
+/* Scaling granularity. */
+#define FP8L_TENSORWISE  0   /* one scale per tensor                          */
+#define FP8L_ROWWISE     1   /* one scale per row of q, one per column of x
+                                (i.e. per row of qt)                         */
+
+/* Largest finite E4M3 value; the scale maps a tensor's amax onto it. */
+#define FP8L_E4M3_MAX    448.0f
+/* Lower clamp of amax in the scale, keeping the scale finite. */
+#define FP8L_AMAX_EPS    1e-12f
+
+/*
+ * Bytes of device workspace fp8_linear_quantize needs for an x of
+ * [rows, cols] with the given scaling (partial maxima of the amax pass).
+ * Returns 0 for invalid arguments.
+ */
+FP8L_API size_t fp8_linear_workspace_bytes(int64_t rows, int64_t cols, int scaling);
+
+/*
+ * Quantize a bf16 matrix to E4M3 with dynamic scaling (amax of the current
+ * tensor; the pages leave the recipe open, this is the reading taken):
+ *
+ *   a        = max |x| over the tensor (tensorwise), or per row of x for
+ *              q and per column of x for qt (rowwise)
+ *   s        = fp32( 448 / max(a, 1e-12) )        one IEEE fp32 division
+ *   q[r][c]  = e4m3_sat_rne( fp32(x[r][c] * s_row[r]) )
+ *   qt[c][r] = e4m3_sat_rne( fp32(x[r][c] * s_col[c]) )
+ *
+ * where e4m3_sat_rne rounds to the nearest E4M3 value (ties to the even
+ * code), clamps magnitudes >= 448 to 448 and keeps the sign (so -0 -> 0x80).
+ * Tensorwise: s_row = s_col = s, so qt is exactly q transposed.
+ *
+ *   x        [rows, cols] bf16 (device, read only)
+ *   q        [rows, cols] e4m3 bytes (device, written)
+ *   qt       [cols, rows] e4m3 bytes (device, written)
+ *   scale    tensorwise [1]; rowwise [rows]  fp32 multipliers s of q
+ *   scale_t  tensorwise [1]; rowwise [cols]  fp32 multipliers s of qt
+ *   amax_out NULL, or tensorwise [1]; rowwise [rows + cols] (rows first)
+ *   workspace / workspace_bytes: >= fp8_linear_workspace_bytes(...) bytes of
+ *            device scratch, owned by the caller, contents undefined on
+ *            entry and exit; must not be shared by calls in flight together.
+ * The stored scale is the multiplier (q = x * s); the GEMMs divide it out.
+ */
+FP8L_API int fp8_linear_quantize(const void *x, int64_t rows, int64_t cols, int scaling,
+                        void *q, void *qt, float *scale, float *scale_t,
+                        float *amax_out, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
+ * Forward GEMM of the linear (out = X . W^T) on the quantized operands:
+ *
+ *   out[m][n] = bf16( fp32( fp32(acc * (1/sx)) * (1/sw) ) ),
+ *   acc       = sum_k value(xq[m][k]) * value(wq[n][k])     (fp32 accumulate)
+ *
+ *   xq [M, K] e4m3 (q of X), sx: tensorwise [1], rowwise [M] (scale of X)
+ *   wq [N, K] e4m3 (q of W), sw: tensorwise [1], rowwise [N] (scale of W)
+ *   out [M, N] bf16 (device, written; rounded to nearest even)
+ * The order of the fp32 additions is unspecified.
+ */
+FP8L_API int fp8_linear_fwd(const void *xq, const float *sx, const void *wq,
+                   const float *sw, int64_t M, int64_t N, int64_t K,
+                   int scaling, void *out, void *stream);
+
+/*
+ * Backward GEMMs of the linear on the quantized operands:
+ *
+ *   grad_x[m][k] = bf16((sum_n dyq[m][n]  * wtq[k][n]) / sdy[m]  / swt[k])
+ *   grad_w[n][k] = bf16((sum_m dytq[n][m] * xtq[k][m]) / sdyt[n] / sxt[k])
+ *
+ * (each "/ s" is a multiplication by the fp32 reciprocal, as in fwd)
+ *
+ *   dyq  [M, N] (q of dY),  sdy  tensorwise [1], rowwise [M]
+ *   dytq [N, M] (qt of dY), sdyt tensorwise [1], rowwise [N]
+ *   wtq  [K, N] (qt of W),  swt  tensorwise [1], rowwise [K]
+ *   xtq  [K, M] (qt of X),  sxt  tensorwise [1], rowwise [K]
+ *   grad_x [M, K] bf16, grad_w [N, K] bf16.
+ * Either output may be NULL to skip that GEMM (its inputs may then be NULL).
+ */
+FP8L_API int fp8_linear_bwd(const void *dyq, const float *sdy, const void *dytq,
+                   const float *sdyt, const void *wtq, const float *swt,
+                   const void *xtq, const float *sxt, int64_t M, int64_t N,
+                   int64_t K, int scaling, void *grad_x, void *grad_w,
+                   void *stream);
+
+/*
+ * The element conversion the quantize kernels use, exposed for testing it on
+ * every fp32 input: out[i] = e4m3_sat_rne(in[i]) (definition above; a NaN
+ * input gives a NaN code).  in: n fp32, out: n bytes, both device pointers.
+ * n >= 0, no multiple-of-16 requirement.
+ */
+FP8L_API int fp8_linear_encode_e4m3(const float *in, uint8_t *out, int64_t n,
+                           void *stream);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+FP8L_API const char *fp8_linear_status_string(int status);
+
+/* Library version and target, e.g. "fp8_linear 0.1 gfx950". */
+FP8L_API const char *fp8_linear_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8_LINEAR_H */

@@ -1,0 +1,144 @@
+"""The C ABI library: it loads, exports every symbol include/fp8_linear.h
+declares, and rejects bad arguments on the host with the documented status
+codes before anything is enqueued.  No compute calls: every case here fails
+validation, so no kernel is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from float8_mixed_precision_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8_linear.h")
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"FP8L_API\s+[\w\s\*]*?\b(fp8_linear_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_symbols() == sorted(ops.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(fp8_linear_\w+)", out))
+    assert set(declared_symbols()) <= exported
+    L = ops.lib()
+    for s in declared_symbols():
+        assert getattr(L, s) is not None
+
+
+def test_status_strings_and_version():
+    assert ops.status_string(0) == "ok"
+    for s in range(1, 6):
+        assert ops.status_string(s) and ops.status_string(s) != "unknown status"
+    assert ops.status_string(99) == "unknown status"
+    assert "gfx950" in ops.fp8_linear_version()
+
+
+def test_workspace_bytes():
+    assert ops.fp8_linear_workspace_bytes(0, 0) == 0
+    assert ops.fp8_linear_workspace_bytes(17, 16) == 0            # invalid shape
+    assert ops.lib().fp8_linear_workspace_bytes(16, 16, 5) == 0    # invalid mode
+    tw = ops.fp8_linear_workspace_bytes(8192, 14336, False)
+    rw = ops.fp8_linear_workspace_bytes(8192, 14336, True)
+    assert 0 < tw < rw and tw % 256 == 0 and rw % 256 == 0
+
+
+# Fake device addresses: validation must reject these calls before any
+# pointer is used.  These tests only run where no GPU is visible.
+A16 = 0x10000          # 16-byte aligned
+A_BAD = 0x10004        # misaligned
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+pytestmark_cpu = pytest.mark.skipif(not _no_gpu(), reason="fake-pointer cases run without a GPU only")
+
+
+def q_call(x=A16, rows=16, cols=16, scaling=0, q=A16, qt=A16, s=A16, st=A16,
+           amax=None, ws=A16, wsb=1 << 20):
+    P = ctypes.c_void_p
+    return ops.lib().fp8_linear_quantize(P(x) if x else None, rows, cols, scaling,
+                                         P(q) if q else None, P(qt) if qt else None,
+                                         P(s) if s else None, P(st) if st else None,
+                                         P(amax) if amax else None, P(ws) if ws else None,
+                                         wsb, None)
+
+
+@pytestmark_cpu
+def test_quantize_rejects_bad_arguments():
+    E = ops
+    assert q_call(scaling=2) == E.FP8L_EINVAL
+    assert q_call(rows=17) == E.FP8L_ESHAPE
+    assert q_call(cols=-16) == E.FP8L_ESHAPE
+    assert q_call(rows=1 << 31) == E.FP8L_ESHAPE
+    assert q_call(x=None) == E.FP8L_EINVAL
+    assert q_call(q=None) == E.FP8L_EINVAL
+    assert q_call(qt=None) == E.FP8L_EINVAL
+    assert q_call(s=None) == E.FP8L_EINVAL
+    assert q_call(st=None) == E.FP8L_EINVAL
+    assert q_call(ws=None) == E.FP8L_EINVAL
+    assert q_call(wsb=0) == E.FP8L_EWORKSPACE
+    assert q_call(rows=8192, cols=4096, wsb=100) == E.FP8L_EWORKSPACE
+    assert q_call(x=A_BAD) == E.FP8L_EALIGN
+    assert q_call(q=A_BAD) == E.FP8L_EALIGN
+    assert q_call(qt=A_BAD) == E.FP8L_EALIGN
+    assert q_call(ws=A_BAD) == E.FP8L_EALIGN
+    assert q_call(s=A16 + 2) == E.FP8L_EALIGN
+    assert q_call(amax=A16 + 1) == E.FP8L_EALIGN
+
+
+@pytestmark_cpu
+def test_gemm_entry_points_reject_bad_arguments():
+    E = ops
+    L = ops.lib()
+    P = ctypes.c_void_p
+
+    def fwd(xq=A16, sx=A16, wq=A16, sw=A16, M=16, N=16, K=16, scaling=0, out=A16):
+        return L.fp8_linear_fwd(P(xq) if xq else None, P(sx) if sx else None,
+                                P(wq) if wq else None, P(sw) if sw else None,
+                                M, N, K, scaling, P(out) if out else None, None)
+
+    assert fwd(scaling=-1) == E.FP8L_EINVAL
+    assert fwd(M=8) == E.FP8L_ESHAPE
+    assert fwd(K=-16) == E.FP8L_ESHAPE
+    assert fwd(xq=None) == E.FP8L_EINVAL
+    assert fwd(sw=None) == E.FP8L_EINVAL
+    assert fwd(out=None) == E.FP8L_EINVAL
+    assert fwd(wq=A_BAD) == E.FP8L_EALIGN
+    assert fwd(out=A_BAD) == E.FP8L_EALIGN
+    assert fwd(sx=A16 + 1) == E.FP8L_EALIGN
+
+    def bwd(gx=A16, gw=A16, dyq=A16, wtq=A_BAD, **kw):
+        return L.fp8_linear_bwd(P(dyq) if dyq else None, P(A16), P(A16), P(A16),
+                                P(wtq) if wtq else None, P(A16), P(A16), P(A16),
+                                kw.get("M", 16), kw.get("N", 16), kw.get("K", 16),
+                                kw.get("scaling", 0), P(gx) if gx else None,
+                                P(gw) if gw else None, None)
+
+    assert bwd(gx=None, gw=None) == E.FP8L_EINVAL
+    assert bwd(N=24) == E.FP8L_ESHAPE
+    assert bwd() == E.FP8L_EALIGN                    # grad_x operands checked
+    assert bwd(wtq=None) == E.FP8L_EINVAL
+    assert bwd(gw=A_BAD, wtq=A16) == E.FP8L_EALIGN   # grad_w output checked
+    assert bwd(scaling=3) == E.FP8L_EINVAL
+
+
+@pytestmark_cpu
+def test_encode_rejects_bad_arguments():
+    L = ops.lib()
+    P = ctypes.c_void_p
+    assert L.fp8_linear_encode_e4m3(P(A16), P(A16), -1, None) == ops.FP8L_ESHAPE
+    assert L.fp8_linear_encode_e4m3(None, P(A16), 4, None) == ops.FP8L_EINVAL
+    assert L.fp8_linear_encode_e4m3(P(A_BAD), P(A16), 4, None) == ops.FP8L_EALIGN
+    assert L.fp8_linear_encode_e4m3(None, None, 0, None) == ops.FP8L_OK   # empty

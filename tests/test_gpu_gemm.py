@@ -1,0 +1,114 @@
+"""GPU parity of the three scaled fp8 GEMMs (fwd, grad_X, grad_W) against the
+oracle on the same fp8 bytes: relative Frobenius <= 1e-3 and every element
+within 2 bf16 ulps plus the room two fp32 summation orders may differ by."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from float8_mixed_precision_amd import ops
+from float8_mixed_precision_amd import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gemm(a, sa, b, sb, rowwise):
+    out = ops.fp8_linear_fwd(G.dev_u8(a), G.dev_f32(sa), G.dev_u8(b), G.dev_f32(sb), rowwise)
+    torch.cuda.synchronize()
+    return G.host(out)
+
+
+def random_operands(m, n, k, rowwise, seed):
+    """fp8 operands as quantize produces them from Gaussian bf16 data."""
+    xa = W.random_bf16(seed, (m, k), 1.0, 0)
+    xb = W.random_bf16(seed, (n, k), 0.02, 1)
+    a, _, sa, _, _ = oracle.quantize(xa, rowwise)
+    b, _, sb, _, _ = oracle.quantize(xb, rowwise)
+    return a, sa, b, sb
+
+
+SHAPES = [(16, 16, 16), (256, 256, 128), (272, 400, 208), (528, 784, 336),
+          (48, 1040, 4112), (1040, 48, 272), (512, 512, 1024)]
+
+
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "%dx%dx%d" % s)
+def test_gemm_full_compare(shape, rowwise):
+    """Every output, on shapes that span several 256x256 tiles and leave
+    ragged M, N and K tails (multiples of 16 only)."""
+    m, n, k = shape
+    a, sa, b, sb = random_operands(m, n, k, rowwise, seed=sum(shape))
+    G.say("gemm", shape, "rowwise", rowwise)
+    got = run_gemm(a, sa, b, sb, rowwise)
+    want = oracle.gemm_tn(a, sa, b, sb)
+    G.gemm_parity(got, want, a, b, sa, sb, label="gemm %s rw=%s" % (shape, rowwise))
+
+
+def test_gemm_extreme_codes():
+    """All-448 operands (largest products, long sums), all-smallest-subnormal
+    operands, and alternating signs (exact cancellation)."""
+    m, n, k = 272, 272, 2064
+    cases = {
+        "max": (np.full((m, k), 0x7E, np.uint8), np.full((n, k), 0x7E, np.uint8)),
+        "min_sub": (np.full((m, k), 0x01, np.uint8), np.full((n, k), 0x81, np.uint8)),
+        "cancel": (np.tile(np.array([0x7E, 0xFE], np.uint8), (m, k // 2)),
+                   np.full((n, k), 0x40, np.uint8)),
+    }
+    for name, (a, b) in cases.items():
+        for sa, sb in ((1.0, 1.0), (448.0, 3.0e-2)):
+            G.say("gemm extreme", name, sa, sb)
+            got = run_gemm(a, np.float32(sa), b, np.float32(sb), False)
+            want = oracle.gemm_tn(a, np.float32(sa), b, np.float32(sb))
+            G.gemm_parity(got, want, a, b, np.float32(sa), np.float32(sb), label=name)
+
+
+def test_gemm_k_zero_and_empty():
+    G.say("gemm K=0 / M=0")
+    a = torch.empty((32, 0), dtype=torch.uint8, device=G.DEV)
+    b = torch.empty((48, 0), dtype=torch.uint8, device=G.DEV)
+    s = G.dev_f32(np.float32(2.0))
+    out = torch.full((32, 48), 7.0, dtype=torch.bfloat16, device=G.DEV)
+    ops.fp8_linear_fwd(a, s, b, s, False, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    # M = 0: nothing to write, must succeed
+    a0 = torch.empty((0, 64), dtype=torch.uint8, device=G.DEV)
+    b0 = torch.zeros((48, 64), dtype=torch.uint8, device=G.DEV)
+    o0 = torch.empty((0, 48), dtype=torch.bfloat16, device=G.DEV)
+    ops.fp8_linear_fwd(a0, s, b0, s, False, o0)
+    torch.cuda.synchronize()
+
+
+def test_gemm_tensorwise_equals_constant_rowwise():
+    m, n, k = 272, 400, 208
+    a, sa, b, sb = random_operands(m, n, k, False, seed=3)
+    G.say("gemm tensorwise vs constant rowwise")
+    t = run_gemm(a, sa, b, sb, False)
+    r = run_gemm(a, np.full(m, sa[0], np.float32), b, np.full(n, sb[0], np.float32), True)
+    assert np.array_equal(t, r)
+
+
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+def test_linear_step_mid_size(rowwise):
+    """One linear through LinearStep (the launch sequence the benchmark times)
+    on a ragged mid-size shape: quantize outputs bit-exact, all three GEMMs
+    in tolerance, every output compared."""
+    M, N, K = 528, 784, 336
+    x = W.random_bf16(11, (M, K), 1.0, 0)
+    w = W.random_bf16(11, (N, K), 0.02, 1)
+    dy = W.random_bf16(11, (M, N), 1e-2, 2)
+    step = ops.LinearStep(G.dev_bf16(x), G.dev_bf16(w), G.dev_bf16(dy), rowwise)
+    G.say("linear step mid", (M, N, K), "rowwise", rowwise)
+    step.run()
+    torch.cuda.synchronize()
+    ox, ow, ody = (oracle.quantize(t, rowwise) for t in (x, w, dy))
+    for name, qz, ref in (("X", step.qx, ox), ("W", step.qw, ow), ("dY", step.qdy, ody)):
+        got = (G.host(qz.q), G.host(qz.qt), G.host(qz.scale), G.host(qz.scale_t), G.host(qz.amax))
+        G.assert_quantize_equal(got, ref, "quantize " + name)
+    out = oracle.gemm_tn(ox[0], ox[2], ow[0], ow[2])
+    G.gemm_parity(G.host(step.out), out, ox[0], ow[0], ox[2], ow[2], label="fwd")
+    gx = oracle.gemm_tn(ody[0], ody[2], ow[1], ow[3])
+    G.gemm_parity(G.host(step.grad_x), gx, ody[0], ow[1], ody[2], ow[3], label="grad_x")
+    gw = oracle.gemm_tn(ody[1], ody[3], ox[1], ox[3])
+    G.gemm_parity(G.host(step.grad_w), gw, ody[1], ox[1], ody[3], ox[3], label="grad_w")

@@ -1,0 +1,79 @@
+"""The whole fp8 linear (quantize X, W, dY; fwd; grad_X; grad_W) at the
+workload sizes, in the launch sequence the benchmark times (LinearStep).
+
+Quantize outputs are compared with the oracle in full, bit for bit.  GEMM
+outputs are compared in full for the tiny workload and, at the full Llama
+sizes, on sampled positions (random ones plus every tile boundary and the
+last row / column) that the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from float8_mixed_precision_amd import ops
+from float8_mixed_precision_amd import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def check_linear(lin, data, rowwise, sampled, seed):
+    M, N, K = lin.M, lin.N, lin.K
+    G.say("linear", lin.name, (M, N, K), "rowwise", rowwise, "upload")
+    step = ops.LinearStep(G.dev_bf16(data["x"]), G.dev_bf16(data["w"]),
+                          G.dev_bf16(data["dy"]), rowwise)
+    G.say("linear", lin.name, "run")
+    step.run()
+    torch.cuda.synchronize()
+    G.say("linear", lin.name, "compare quantize")
+    ref = {}
+    for name, qz in (("x", step.qx), ("w", step.qw), ("dy", step.qdy)):
+        r = oracle.quantize(data[name], rowwise)
+        got = (G.host(qz.q), G.host(qz.qt), G.host(qz.scale), G.host(qz.scale_t),
+               G.host(qz.amax))
+        G.assert_quantize_equal(got, r, "%s quantize %s" % (lin.name, name))
+        ref[name] = r
+    ox, ow, ody = ref["x"], ref["w"], ref["dy"]
+    gemms = (("fwd", step.out, ox[0], ox[2], ow[0], ow[2]),
+             ("grad_x", step.grad_x, ody[0], ody[2], ow[1], ow[3]),
+             ("grad_w", step.grad_w, ody[1], ody[3], ox[1], ox[3]))
+    for name, out_t, a, sa, b, sb in gemms:
+        m, n = a.shape[0], b.shape[0]
+        G.say("linear", lin.name, "compare", name, (m, n, a.shape[1]))
+        if sampled:
+            ii, jj = G.sample_indices(m, n, 6000, seed)
+            got = G.host(out_t[torch.from_numpy(ii).to(G.DEV), torch.from_numpy(jj).to(G.DEV)])
+            want = oracle.gemm_tn_sampled(a, sa, b, sb, ii, jj)
+            G.gemm_parity(got, want, a, b, sa, sb, ii, jj, label="%s %s" % (lin.name, name))
+        else:
+            G.gemm_parity(G.host(out_t), oracle.gemm_tn(a, sa, b, sb), a, b, sa, sb,
+                          label="%s %s" % (lin.name, name))
+    del step
+    torch.cuda.empty_cache()
+
+
+def test_tiny_workload_full():
+    wl = W.WORKLOADS["tiny_tw"]
+    data = W.generate(wl)
+    for lin, d in zip(wl.linears, data):
+        check_linear(lin, d, wl.rowwise, sampled=False, seed=0)
+
+
+FULL = [("attn8b_tw", 0), ("ffn8b_tw", 0), ("ffn8b_tw", 2), ("ffn70b_tw", 0), ("outlier_rw", 0)]
+
+
+@pytest.mark.parametrize("name,li", FULL, ids=lambda v: str(v))
+def test_full_size_linear(name, li):
+    wl = W.WORKLOADS[name]
+    lin = wl.linears[li]
+    data = W.generate_linear(wl, li)
+    check_linear(lin, data, wl.rowwise, sampled=True, seed=li + 1)
+
+
+def test_rowwise_at_headline_shape_with_gaussian_inputs():
+    """Rowwise scaling on the plain 8B FFN w1 inputs (the outlier case covers
+    Student-t activations)."""
+    wl = W.WORKLOADS["ffn8b_tw"]
+    lin = wl.linears[0]
+    data = W.generate_linear(wl, 0)
+    check_linear(lin, data, True, sampled=True, seed=9)

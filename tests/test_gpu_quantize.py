@@ -1,0 +1,170 @@
+"""GPU parity of the quantize path (amax -> scale -> saturating E4M3 cast and
+transpose) against the oracle: bytes and scales bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from float8_mixed_precision_amd import ops
+from float8_mixed_precision_amd import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def test_encode_band_exhaustive():
+    """Device conversion on every positive fp32 pattern of exponents 115..136
+    (where E4M3 rounding happens), and their negatives."""
+    for e in range(115, 137, 2):
+        G.say("encode exponents", e, e + 1)
+        bits = np.arange(e << 23, (e + 2) << 23, dtype=np.uint32)
+        y = bits.view(np.float32)
+        yd = torch.from_numpy(y).to(G.DEV)
+        got = G.host(ops.fp8_linear_encode_e4m3(yd))
+        want = oracle.e4m3_encode(y)
+        assert np.array_equal(got, want), "exponent %d" % e
+        got_neg = G.host(ops.fp8_linear_encode_e4m3(-yd))
+        assert np.array_equal(got_neg, want ^ 0x80), "negative, exponent %d" % e
+
+
+def test_encode_random_and_special():
+    rng = np.random.default_rng(21)
+    bits = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    special = np.array([0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00000,
+                        1, 0x80000001, 0x7F7FFFFF, 0xFF7FFFFF, 0x43E00000, 0x43E80000,
+                        0x3A800000, 0x3AC00000], np.uint32)
+    y = np.concatenate([bits, special]).view(np.float32)
+    for n in (y.size, 3, 1):          # also tails that are not a multiple of 4
+        G.say("encode random", n)
+        got = G.host(ops.fp8_linear_encode_e4m3(torch.from_numpy(y[:n].copy()).to(G.DEV)))
+        want = oracle.e4m3_encode(y[:n])
+        nan = np.isnan(y[:n])
+        assert np.all((got[nan] & 0x7F) == 0x7F)
+        assert np.array_equal(got[~nan], want[~nan])
+
+
+def all_finite_bf16(rows=256):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = (h & 0x7F80) != 0x7F80
+    h = np.where(fin, h, 0).astype(np.uint16)
+    return h.reshape(rows, -1)
+
+
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+def test_quantize_every_bf16_value(rowwise):
+    """Every finite bf16 pattern, with the largest magnitude forced to several
+    levels so that the scaled values sweep the whole E4M3 range, including
+    subnormal results and bf16 subnormal inputs."""
+    base = all_finite_bf16()
+    f = oracle.bf16_to_f32(base)
+    for lim in (3.0e38, 1e5, 448.0, 1.0, 1e-3, 1e-30, 1e-38):
+        x = np.where(np.abs(f) <= lim, base, 0).astype(np.uint16)
+        G.say("quantize all-bf16 lim", lim, "rowwise", rowwise)
+        got = G.gpu_quantize(x, rowwise)
+        ref = oracle.quantize(x, rowwise)
+        G.assert_quantize_equal(got, ref, "all-bf16 lim %g" % lim)
+        # transposed layout too (rows and columns swap roles)
+        got = G.gpu_quantize(np.ascontiguousarray(x.T), rowwise)
+        ref = oracle.quantize(np.ascontiguousarray(x.T), rowwise)
+        G.assert_quantize_equal(got, ref, "all-bf16^T lim %g" % lim)
+
+
+SHAPES = [(16, 16), (256, 256), (272, 400), (48, 4112), (1040, 80), (528, 784), (144, 2064)]
+
+
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "%dx%d" % s)
+def test_quantize_shapes(shape, rowwise):
+    """Ragged shapes (not multiples of the 64x256 amax or 128x128 cast tiles)
+    and several distributions."""
+    rng = np.random.default_rng(hash(shape) % 1000)
+    cases = {
+        "normal": W.random_bf16(3, shape, 1.0, 0),
+        "weights": W.random_bf16(3, shape, 0.02, 1),
+        "student_t": W.to_bf16_bits(rng.standard_t(3, size=shape).astype(np.float32)),
+    }
+    for name, x in cases.items():
+        G.say("quantize", shape, name, "rowwise", rowwise)
+        G.assert_quantize_equal(G.gpu_quantize(x, rowwise), oracle.quantize(x, rowwise),
+                                "%s %s" % (shape, name))
+
+
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+def test_quantize_special_tensors(rowwise):
+    shape = (272, 400)
+    rng = np.random.default_rng(5)
+    x = W.random_bf16(4, shape, 1.0, 2)
+    cases = {}
+    cases["zeros"] = np.zeros(shape, np.uint16)
+    one = np.zeros(shape, np.uint16)
+    one[100, 37] = 0x3F80
+    cases["single"] = one
+    cases["constant"] = np.full(shape, 0xC0A0, np.uint16)
+    big = x.copy()
+    big[7, 300] = 0x7F00                                   # ~1.7e38 outlier
+    cases["outlier"] = big
+    sub = x.copy()
+    sub[:32] = W.to_bf16_bits(rng.standard_normal((32, shape[1])).astype(np.float32) * 1e-39)
+    cases["subnormal_rows"] = sub
+    zr = x.copy()
+    zr[16:32] = 0
+    zr[:, 64:80] = 0
+    zr[200] = 0x8000                                       # a row of -0
+    cases["zero_rows_cols"] = zr
+    neg = x.copy()
+    neg[np.abs(oracle.bf16_to_f32(neg)) < 0.5] = 0x8000
+    cases["neg_zeros"] = neg
+    for name, c in cases.items():
+        G.say("quantize special", name, "rowwise", rowwise)
+        G.assert_quantize_equal(G.gpu_quantize(c, rowwise), oracle.quantize(c, rowwise), name)
+
+
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+def test_quantize_non_finite_surfaces_in_amax(rowwise):
+    """NaN / inf inputs are no error: they must show up in amax (and not
+    crash); the bytes are unspecified."""
+    shape = (128, 256)
+    x = W.random_bf16(6, shape, 1.0, 3)
+    xn = x.copy()
+    xn[5, 9] = 0x7FC0                                      # NaN
+    xi = x.copy()
+    xi[77, 200] = 0xFF80                                   # -inf
+    G.say("quantize non-finite rowwise", rowwise)
+    _, _, _, _, am = G.gpu_quantize(xn, rowwise)
+    assert np.isnan(am[0] if not rowwise else am[5]) and (not rowwise or np.isnan(am[shape[0] + 9]))
+    _, _, _, _, am = G.gpu_quantize(xi, rowwise)
+    if rowwise:
+        assert np.isposinf(am[77]) and np.isposinf(am[shape[0] + 200])
+        assert np.all(np.isfinite(np.delete(am, [77, shape[0] + 200])))
+    else:
+        assert np.isposinf(am[0])
+
+
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+@pytest.mark.parametrize("shape", [(0, 0), (0, 32), (48, 0)], ids=lambda s: "%dx%d" % s)
+def test_quantize_empty(shape, rowwise):
+    """An empty matrix is valid: scales of the empty set (amax 0 ->
+    448 / 1e-12), nothing else written."""
+    G.say("quantize empty", shape, rowwise)
+    x = torch.empty(shape, dtype=torch.bfloat16, device=G.DEV)
+    qz = ops.fp8_linear_quantize(x, rowwise)
+    torch.cuda.synchronize()
+    s_empty = oracle.scale_from_amax(0.0)
+    if rowwise:
+        assert np.all(G.host(qz.scale) == s_empty) and np.all(G.host(qz.scale_t) == s_empty)
+        assert np.all(G.host(qz.amax) == 0)
+    else:
+        assert G.host(qz.scale)[0] == s_empty and G.host(qz.amax)[0] == 0
+
+
+def test_quantize_scaled_max_maps_to_448():
+    """Invariant on the device: the element(s) holding the amax encode to
+    +-448 (0x7E / 0xFE)."""
+    x = W.random_bf16(7, (528, 784), 1.0, 4)
+    f = oracle.bf16_to_f32(x)
+    q, qt, s, st, am = G.gpu_quantize(x, False)
+    hit = np.abs(f) == np.abs(f).max()
+    assert np.all((q[hit] & 0x7F) == 0x7E) and np.all((qt.T[hit] & 0x7F) == 0x7E)
+    q, qt, s, st, am = G.gpu_quantize(x, True)
+    assert np.all((q[np.abs(f) == np.abs(f).max(axis=1, keepdims=True)] & 0x7F) == 0x7E)
+    assert np.all((qt.T[np.abs(f) == np.abs(f).max(axis=0, keepdims=True)] & 0x7F) == 0x7E)
