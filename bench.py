@@ -42,7 +42,23 @@ def parse():
                    help="skip the CPU oracle timing (e.g. under a profiler)")
     p.add_argument("--cpu-rows", type=int, default=128,
                    help="output rows per GEMM in the CPU oracle sample")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="only run 3 plain device copies of this many bytes (the "
+                        "calibration kernel for HBM byte counters) and exit")
     return p.parse_args()
+
+
+def copy_calibration(nbytes: int):
+    """Three launches of a plain streaming elementwise kernel (fp32 negate,
+    out of place) over nbytes: nbytes read and nbytes written per launch,
+    each touched once, so its HBM byte counters have a known answer."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
 
 
 def gemm_source_hash() -> str:
@@ -113,6 +129,9 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
 
     import numpy as np
     import torch

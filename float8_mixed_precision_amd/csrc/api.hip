@@ -13,6 +13,13 @@ bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 // stays in range (addresses are formed in 64 bits), and a matrix at 2^40
 // elements so that grid sizes fit in 32 bits.
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
+// GEMM operands and outputs are addressed through buffer resources with
+// 32-bit byte offsets: each must stay below 2^31 bytes.
+constexpr int64_t kMaxGemmBytes = ((int64_t)1 << 31) - 1;
+
+bool bad_gemm_sizes(int64_t m, int64_t n, int64_t k) {
+  return m * k > kMaxGemmBytes || n * k > kMaxGemmBytes || 2 * m * n > kMaxGemmBytes;
+}
 
 // C[m,n] = A[m,k] . B[n,k]^T: a pointer may be NULL only where its matrix
 // is empty; the scales are read whenever an output element is written.
@@ -68,7 +75,7 @@ int fp8_linear_fwd(const void *xq, const float *sx, const void *wq,
                    int scaling, void *out, void *stream) {
   if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return FP8L_EINVAL;
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8L_ESHAPE;
-  if (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems) return FP8L_ESHAPE;
+  if (bad_gemm_sizes(M, N, K)) return FP8L_ESHAPE;
   int s = check_gemm_operands(xq, sx, wq, sw, out, M, N, K);
   if (s != FP8L_OK) return s;
   const int vec = scaling == FP8L_ROWWISE;
@@ -86,7 +93,8 @@ int fp8_linear_bwd(const void *dyq, const float *sdy, const void *dytq,
                    void *stream) {
   if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return FP8L_EINVAL;
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8L_ESHAPE;
-  if (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems) return FP8L_ESHAPE;
+  // grad_x: [M,K] from [M,N] x [K,N]; grad_w: [N,K] from [N,M] x [K,M]
+  if (bad_gemm_sizes(M, K, N) || bad_gemm_sizes(N, K, M)) return FP8L_ESHAPE;
   if (!grad_x && !grad_w) return FP8L_EINVAL;
   int s;
   if (grad_x && (s = check_gemm_operands(dyq, sdy, wtq, swt, grad_x, M, K, N)) != FP8L_OK)

@@ -28,7 +28,9 @@
  *    asynchronously on it; results are ready when the stream reaches them.
  *    Calls on different streams may run concurrently if their buffers do not
  *    overlap.
- *  - Dimensions must be >= 0 and multiples of 16 (FP8L_ESHAPE otherwise).
+ *  - Dimensions must be >= 0 and multiples of 16 (FP8L_ESHAPE otherwise);
+ *    every fp8 GEMM operand and every bf16 GEMM output must be smaller than
+ *    2^31 bytes.
  *    A zero dimension is an empty matrix: the call is valid and writes only
  *    what its definition gives (scales of the empty set, zero outputs).
  *  - Argument errors are detected on the host before anything is enqueued
