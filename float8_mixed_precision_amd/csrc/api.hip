@@ -79,7 +79,7 @@ int fp8_linear_fwd(const void *xq, const float *sx, const void *wq,
   int s = check_gemm_operands(xq, sx, wq, sw, out, M, N, K);
   if (s != FP8L_OK) return s;
   const int vec = scaling == FP8L_ROWWISE;
-  hipError_t e = fp8l::gemm_launch(static_cast<const uint8_t *>(xq), sx, vec,
+  hipError_t e = fp8l::gemm_launch(static_cast<const uint8_t *>(xq), sx,
                                    static_cast<const uint8_t *>(wq), sw, vec, M, N, K,
                                    static_cast<uint16_t *>(out),
                                    static_cast<hipStream_t>(stream));
@@ -105,11 +105,11 @@ int fp8_linear_bwd(const void *dyq, const float *sdy, const void *dytq,
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (grad_x)  // [M,K] = dYq[M,N] . WTq[K,N]^T
-    e = fp8l::gemm_launch(static_cast<const uint8_t *>(dyq), sdy, vec,
+    e = fp8l::gemm_launch(static_cast<const uint8_t *>(dyq), sdy,
                           static_cast<const uint8_t *>(wtq), swt, vec, M, K, N,
                           static_cast<uint16_t *>(grad_x), st);
   if (e == hipSuccess && grad_w)  // [N,K] = dYTq[N,M] . XTq[K,M]^T
-    e = fp8l::gemm_launch(static_cast<const uint8_t *>(dytq), sdyt, vec,
+    e = fp8l::gemm_launch(static_cast<const uint8_t *>(dytq), sdyt,
                           static_cast<const uint8_t *>(xtq), sxt, vec, N, K, M,
                           static_cast<uint16_t *>(grad_w), st);
   return e == hipSuccess ? FP8L_OK : FP8L_EHIP;

@@ -51,10 +51,10 @@ hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
 hipError_t encode_launch(const float *in, uint8_t *out, int64_t n,
                          hipStream_t stream);
 
-// C[M,N] (bf16) = (A[M,K] . B[N,K]^T) * (1/sa) * (1/sb); sa has M entries
-// when a_vec, else 1; sb has N entries when b_vec, else 1.
-hipError_t gemm_launch(const uint8_t *A, const float *sa, int a_vec,
-                       const uint8_t *B, const float *sb, int b_vec, int64_t M,
-                       int64_t N, int64_t K, uint16_t *C, hipStream_t stream);
+// C[M,N] (bf16) = (A[M,K] . B[N,K]^T) * (1/sa) * (1/sb); with rowwise, sa
+// has M entries and sb N entries, else one each.
+hipError_t gemm_launch(const uint8_t *A, const float *sa, const uint8_t *B,
+                       const float *sb, int rowwise, int64_t M, int64_t N,
+                       int64_t K, uint16_t *C, hipStream_t stream);
 
 }  // namespace fp8l

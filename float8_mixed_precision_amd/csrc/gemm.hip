@@ -12,44 +12,55 @@
 //
 // Design (CDNA4; one 256-thread workgroup per CU, 1 wave per SIMD):
 //  - Output tile 256 x 256; 4 wave64s in a 2 x 2 grid own 128 x 128 each =
-//    4 x 4 tiles of v_mfma_f32_32x32x64_f8f6f4 (format 0 = E4M3 for both
-//    operands, no block scales).  A wave's 256 fp32 accumulators live in
-//    AGPRs; its operand fragments are double-buffered in VGPRs.
-//  - K advances 128 bytes per stage, so every LDS row is one full 128-byte
-//    cache line of a global row: loads of whole lines run at about twice
-//    the per-CU rate of half lines.  Two 64 KB stages (A slab 256 x 128 B,
-//    B slab 256 x 128 B) are filled by buffer_load_dwordx4 ... lds (global
-//    to LDS without VGPRs); each wave-instruction moves 8 rows x 128 B.
-//  - A stage is two MFMA k-steps of 64 bytes.  Per k-tile t:
-//      half-step 0: 16 MFMAs on k-step (t,0), interleaved with the reads of
-//                   (t,1)'s fragments from stage t%2;
-//      wait for this wave's DMA of k-tile t+1, one barrier (everyone's DMA
-//      landed, everyone finished reading stage t%2);
-//      half-step 1: 16 MFMAs on (t,1), interleaved with the reads of
-//                   (t+1,0)'s fragments from the other stage and with the
-//                   16 DMA transfers of k-tile t+2 into stage t%2.
-//    A DMA thus has two half-steps to land, and the only wait is vmcnt(0).
+//    8 x 8 blocks of v_mfma_f32_16x16x128_f8f6f4 (format 0 = E4M3 for both
+//    operands, no block scales).  Under a power-limited clock this shape
+//    sustains about 16% more throughput than the 32x32x64 form on the same
+//    data (measured: 1.97 vs 1.70 GHz with normal-distributed operands).
+//    A wave's 256 fp32 accumulators live in AGPRs.
+//  - K advances 128 bytes per stage, which is one MFMA k-step and one full
+//    128-byte cache line of every global row: whole lines load at about
+//    twice the per-CU rate of half lines.  Two 64 KB stages (A slab
+//    256 x 128 B, B slab 256 x 128 B) are filled by buffer_load_dwordx4 ...
+//    lds (global to LDS without VGPRs); each instruction moves 8 rows x 128 B.
+//  - Fragments: 8 A and 8 B per k-tile (16 rows x 128 B each, 8 VGPRs per
+//    lane), 128 VGPRs in all, each refilled as soon as it falls free.  The
+//    64 MFMAs of k-tile t run in two halves ordered by B fragment:
+//      first half:  A0-3 x B0..B7; reads A4-7(t) and B7(t)
+//      -- wait for this wave's DMA of k-tile t+1 and its reads; barrier --
+//      second half: A4-7 x B0..B7; reads A0-3(t+1) and each B_j(t+1) right
+//                   after the last use of B_j(t), and issues the 16 DMA
+//                   instructions of k-tile t+2 into t's stage, one every
+//                   other MFMA
+//    Every fragment read is issued about 28-32 MFMAs (~1000 cycles) before
+//    its first use: with one wave per SIMD, LDS reads are latency-bound
+//    (measured ~110 B/clk/CU at 4 waves, ~210 at 8), and a shorter lead
+//    stalls the MFMAs.  DMA instructions are spread out because the
+//    global->LDS path sustains ~54-64 B/clk/CU, so a burst of them blocks
+//    issue.  There is one barrier per k-tile.
 //  - Chunk c (16 B) of LDS row r sits at c ^ h(r), h(r) = (r & 7) ^
-//    ((r >> 3) & 1): conflict-free for the 32-row fragment reads whether a
+//    ((r >> 3) & 1): conflict-free for the 16-row fragment reads whether a
 //    ds_read_b128 phase serves 8 lanes / 128 B or 16 lanes / 256 B.  The
 //    swizzle is applied on the global side of the DMA (which writes each
 //    instruction's 64 x 16 B to consecutive LDS addresses).
+//  - Operand lanes: lane l holds row l % 16 of a fragment and 32 bytes of
+//    its k-range, chunks 2 (l / 16) and 2 (l / 16) + 1 (any assignment of k
+//    to lanes works that is the same for both operands).
 //  - M, N and K tails: rows past M / N and 16-byte chunks past K are read
 //    through buffer offsets past the buffer size, which return zeros.
 //  - The MFMA's first operand is the B (n) fragment, the second the A (m)
-//    fragment, so a lane holds 4 consecutive n of one m.  The epilogue
-//    scales, rounds to bf16 (v_cvt_pk_bf16_f32, round to nearest even) and
-//    stages the 128 x 128 tile in LDS to write whole 256-byte rows with
-//    16-byte buffer stores (out-of-range stores are dropped by the buffer
-//    bounds check).
+//    fragment: output register r of lane l is n = 4 (l / 16) + r, m = l % 16
+//    of its 16 x 16 block, so a lane holds 4 consecutive n of one m.  The
+//    epilogue scales, rounds to bf16 (v_cvt_pk_bf16_f32, round to nearest
+//    even) and stages the 128 x 128 tile in LDS to write whole 256-byte rows
+//    with 16-byte buffer stores (out-of-range stores are dropped by the
+//    buffer bounds check).
 //  - Workgroups are renumbered so that each XCD receives one contiguous
 //    range of a grouped tile order (GROUP_M tile-rows at a time), for L2
 //    reuse.
 //
-// Accumulation precision of the instruction (measured on gfx950): products
-// are exact; the products of each group of 8 consecutive k are summed in a
-// fixed-point window of about 13-14 bits below the group's largest product,
-// and the group sums are then added to the accumulator at fp32 precision.
+// The instruction's products are exact and its sums are formed in fp32-class
+// precision in an order of its own; the result differs from a sequential
+// fp32 sum by rounding-order effects only.
 #include "fp8l_internal.h"
 
 namespace fp8l {
@@ -61,20 +72,21 @@ constexpr int BK = 128;                  // fp8 elements (bytes) of K per stage
 constexpr int THREADS = 256;
 constexpr int WM = 128;                  // rows per wave
 constexpr int WN = 128;                  // cols per wave
-constexpr int TM = WM / 32;              // MFMA tiles along M per wave
-constexpr int TN = WN / 32;              // MFMA tiles along N per wave
+constexpr int FR = 16;                   // rows per fragment
+constexpr int NF = WM / FR;              // fragments per operand per wave (8)
 constexpr int SLAB = BM * BK;            // 32 KB
 constexpr int STAGE_BYTES = 2 * SLAB;    // 64 KB: A slab, then B slab
 constexpr int EP_STRIDE = 272;           // staged output row: 256 B + 16 B pad
 constexpr int EP_WAVE = WM * EP_STRIDE;  // staged output of one wave
-constexpr int LDS_BYTES = 2 * STAGE_BYTES > 4 * EP_WAVE ? 2 * STAGE_BYTES : 4 * EP_WAVE;
+constexpr int INV_OFF = 2 * STAGE_BYTES > 4 * EP_WAVE ? 2 * STAGE_BYTES : 4 * EP_WAVE;
+constexpr int INV_BYTES = (BM + BN) * 4;  // rowwise: 1/sa of the tile's rows, 1/sb of its cols
 constexpr int GROUP_M = 8;
 constexpr int NUM_XCD = 8;
 constexpr uint32_t OOB = 0x80000000u;    // operand offset that reads as zero
 constexpr uint32_t OOB_C = 0xFFFFFF00u;  // output offset that is dropped
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // s_waitcnt with only one counter constrained (gfx9 encoding: vmcnt[3:0] in
@@ -84,6 +96,15 @@ __device__ __forceinline__ void wait_vmcnt0() {
 }
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier that is also a compiler barrier for memory accesses, so
+// no LDS read or write is moved across it (the barrier intrinsic alone does
+// not order plain loads and stores).
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // One 16-byte global -> LDS transfer per lane: lane i's bytes land at LDS
@@ -120,24 +141,33 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m,
   tn = in_group / gm;
 }
 
-template <bool KFULL>   // K % 128 == 0: no K tail, no per-chunk K check
+// KFULL: K % 128 == 0 (no K tail, no per-chunk K check).  RW: rowwise
+// scales (sa[M], sb[N]) instead of one scale per operand.
+template <bool KFULL, bool RW>
 __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
-    const uint8_t *__restrict__ A, const float *__restrict__ sa, int a_vec,
-    const uint8_t *__restrict__ B, const float *__restrict__ sb, int b_vec,
+    const uint8_t *__restrict__ A, const float *__restrict__ sa,
+    const uint8_t *__restrict__ B, const float *__restrict__ sb,
     int M, int N, int K, uint16_t *__restrict__ C, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[INV_OFF + (RW ? INV_BYTES : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1;
   const int wn = wave & 1;
-  const int kh = lane >> 5;            // which 32-byte half of a 64-byte k-step
 
   int tmi, tni;
   tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tmi, tni);
   const int m0 = tmi * BM;
   const int n0 = tni * BN;
+
+  // rowwise: the tile's 256 + 256 reciprocal scales, one of each per thread,
+  // into their own LDS region (read after the main loop's last barrier)
+  if (RW) {
+    float *inv = reinterpret_cast<float *>(lds + INV_OFF);
+    inv[tid] = m0 + tid < M ? 1.0f / sa[m0 + tid] : 0.f;
+    inv[BM + tid] = n0 + tid < N ? 1.0f / sb[n0 + tid] : 0.f;
+  }
 
   const __amdgpu_buffer_rsrc_t rsA =
       __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, M * K, 0x00020000);
@@ -175,106 +205,189 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
                           ((Q) >= 8 ? SLAB : 0) + ((Q) & 7) * 1024);              \
     dma16((Q) >= 8 ? rsB : rsA, dst_, kok_ ? voff[Q] : OOB, k0_);                 \
   } while (0)
-#define FP8L_DMAALL(ST, KT)                                                       \
-  FP8L_DMA1(ST, KT, 0); FP8L_DMA1(ST, KT, 1); FP8L_DMA1(ST, KT, 2);               \
-  FP8L_DMA1(ST, KT, 3); FP8L_DMA1(ST, KT, 4); FP8L_DMA1(ST, KT, 5);               \
-  FP8L_DMA1(ST, KT, 6); FP8L_DMA1(ST, KT, 7); FP8L_DMA1(ST, KT, 8);               \
-  FP8L_DMA1(ST, KT, 9); FP8L_DMA1(ST, KT, 10); FP8L_DMA1(ST, KT, 11);             \
-  FP8L_DMA1(ST, KT, 12); FP8L_DMA1(ST, KT, 13); FP8L_DMA1(ST, KT, 14);            \
-  FP8L_DMA1(ST, KT, 15);
 
-  // ---- fragment reads: row = wm*128 + i*32 + lane%32 (h(row) depends only
-  // on lane%16); k-step kk reads logical chunks kk*4 + kh*2 + {0, 1}
+  // ---- fragment reads: fragment f of A is rows wm*128 + f*16 + lane%16;
+  // lane l reads logical chunks 2(l/16) and 2(l/16)+1; h(row) depends only
+  // on lane%16
   const int hr = (lane & 7) ^ ((lane >> 3) & 1);
-  const int fArow = (wm * WM + (lane & 31)) * BK;
-  const int fBrow = SLAB + (wn * WN + (lane & 31)) * BK;
-  const int fc00 = (((0 * 4 + kh * 2 + 0) ^ hr) << 4);
-  const int fc01 = (((0 * 4 + kh * 2 + 1) ^ hr) << 4);
-  const int fc10 = (((1 * 4 + kh * 2 + 0) ^ hr) << 4);
-  const int fc11 = (((1 * 4 + kh * 2 + 1) ^ hr) << 4);
+  const int g4 = lane >> 4;
+  const int fArow = (wm * WM + (lane & 15)) * BK;
+  const int fBrow = SLAB + (wn * WN + (lane & 15)) * BK;
+  const int fc0 = ((2 * g4) ^ hr) << 4;
+  const int fc1 = ((2 * g4 + 1) ^ hr) << 4;
 
-  v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-  v16f acc[TN][TM];
+  v8i fa[NF], fb[NF];
+  v4f acc[NF][NF];   // [j: n block][i: m block]
 #pragma unroll
-  for (int j = 0; j < TN; ++j)
+  for (int j = 0; j < NF; ++j)
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+    for (int i = 0; i < NF; ++i) acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // 16-byte piece Q (0..15) of a fragment set, in the order the MFMAs
-  // consume them: B0, A0, A1, A2, A3, B1, B2, B3 (low, high halves)
-#define FP8L_READ1(STAGE, KK, Q, NA, NB)                                          \
+  // half H (0: chunk 2(l/16), 1: the next) of fragment F of operand X
+#define FP8L_RD(STAGE, X, F, H)                                                   \
   do {                                                                            \
-    constexpr int p_ = (Q) / 2, h_ = (Q) % 2;                                     \
-    constexpr bool isb_ = p_ == 0 || p_ >= 5;                                     \
-    constexpr int f_ = p_ == 0 ? 0 : (p_ <= 4 ? p_ - 1 : p_ - 4);                 \
-    const int co_ = (KK) == 0 ? (h_ ? fc01 : fc00) : (h_ ? fc11 : fc10);          \
-    const uint8_t *src_ = lds + (STAGE) * STAGE_BYTES + (isb_ ? fBrow : fArow) +  \
-                          f_ * 32 * BK + co_;                                     \
+    const uint8_t *src_ = lds + (STAGE) * STAGE_BYTES +                           \
+                          ((X) ? fBrow : fArow) + (F) * FR * BK + ((H) ? fc1 : fc0); \
     const v4u v_ = *reinterpret_cast<const v4u *>(src_);                          \
-    if (isb_) { NB[f_][4 * h_] = (int)v_.x; NB[f_][4 * h_ + 1] = (int)v_.y;       \
-                NB[f_][4 * h_ + 2] = (int)v_.z; NB[f_][4 * h_ + 3] = (int)v_.w; } \
-    else      { NA[f_][4 * h_] = (int)v_.x; NA[f_][4 * h_ + 1] = (int)v_.y;       \
-                NA[f_][4 * h_ + 2] = (int)v_.z; NA[f_][4 * h_ + 3] = (int)v_.w; } \
+    if (X) { fb[F][4 * (H)] = (int)v_.x; fb[F][4 * (H) + 1] = (int)v_.y;          \
+             fb[F][4 * (H) + 2] = (int)v_.z; fb[F][4 * (H) + 3] = (int)v_.w; }    \
+    else   { fa[F][4 * (H)] = (int)v_.x; fa[F][4 * (H) + 1] = (int)v_.y;          \
+             fa[F][4 * (H) + 2] = (int)v_.z; fa[F][4 * (H) + 3] = (int)v_.w; }    \
   } while (0)
-#define FP8L_MFMA1(Q, CA, CB)                                                     \
-  do {                                                                            \
-    constexpr int j_ = (Q) / 4, i_ = (Q) % 4;                                     \
-    acc[j_][i_] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                \
-        CB[j_], CA[i_], acc[j_][i_], 0, 0, 0, 0, 0, 0);                           \
-  } while (0)
-  // slot Q of half-step 0 / 1; sched_barrier keeps the interleaving
-#define FP8L_SLOT0(Q, ST)                                                         \
-  FP8L_MFMA1(Q, fa0, fb0); FP8L_READ1(ST, 1, Q, fa1, fb1);                        \
-  __builtin_amdgcn_sched_barrier(0);
-#define FP8L_SLOT1(Q, ST, STN, KT)                                                \
-  FP8L_MFMA1(Q, fa1, fb1); FP8L_READ1(STN, 0, Q, fa0, fb0); FP8L_DMA1(ST, KT, Q); \
-  __builtin_amdgcn_sched_barrier(0);
-#define FP8L_READ0(Q) FP8L_READ1(0, 0, Q, fa0, fb0);
+#define FP8L_MF(J, I)                                                             \
+  acc[J][I] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                   \
+      fb[J], fa[I], acc[J][I], 0, 0, 0, 0, 0, 0)
+  // slot S (0..31) of a half runs MFMA (B frag S/4) x (A frag I0 + S%4)
+  // plus the memory instructions listed for it
+#define FP8L_M(S, I0) FP8L_MF((S) / 4, (I0) + (S) % 4);
+#define FP8L_E() __builtin_amdgcn_sched_barrier(0);
+#define FP8L_H1(ST) \
+  FP8L_M(0, 0) FP8L_RD(ST, 0, 4, 0); FP8L_E() \
+  FP8L_M(1, 0) FP8L_RD(ST, 0, 4, 1); FP8L_E() \
+  FP8L_M(2, 0) FP8L_RD(ST, 0, 5, 0); FP8L_E() \
+  FP8L_M(3, 0) FP8L_RD(ST, 0, 5, 1); FP8L_E() \
+  FP8L_M(4, 0) FP8L_RD(ST, 0, 6, 0); FP8L_E() \
+  FP8L_M(5, 0) FP8L_RD(ST, 0, 6, 1); FP8L_E() \
+  FP8L_M(6, 0) FP8L_RD(ST, 0, 7, 0); FP8L_E() \
+  FP8L_M(7, 0) FP8L_RD(ST, 0, 7, 1); FP8L_E() \
+  FP8L_M(8, 0) FP8L_RD(ST, 1, 7, 0); FP8L_E() \
+  FP8L_M(9, 0) FP8L_RD(ST, 1, 7, 1); FP8L_E() \
+  FP8L_M(10, 0) FP8L_E() \
+  FP8L_M(11, 0) FP8L_E() \
+  FP8L_M(12, 0) FP8L_E() \
+  FP8L_M(13, 0) FP8L_E() \
+  FP8L_M(14, 0) FP8L_E() \
+  FP8L_M(15, 0) FP8L_E() \
+  FP8L_M(16, 0) FP8L_E() \
+  FP8L_M(17, 0) FP8L_E() \
+  FP8L_M(18, 0) FP8L_E() \
+  FP8L_M(19, 0) FP8L_E() \
+  FP8L_M(20, 0) FP8L_E() \
+  FP8L_M(21, 0) FP8L_E() \
+  FP8L_M(22, 0) FP8L_E() \
+  FP8L_M(23, 0) FP8L_E() \
+  FP8L_M(24, 0) FP8L_E() \
+  FP8L_M(25, 0) FP8L_E() \
+  FP8L_M(26, 0) FP8L_E() \
+  FP8L_M(27, 0) FP8L_E() \
+  FP8L_M(28, 0) FP8L_E() \
+  FP8L_M(29, 0) FP8L_E() \
+  FP8L_M(30, 0) FP8L_E() \
+  FP8L_M(31, 0) FP8L_E()
+#define FP8L_H2(STN, DST, KT) \
+  FP8L_M(0, 4) FP8L_RD(STN, 0, 0, 0); FP8L_E() \
+  FP8L_M(1, 4) FP8L_DMA1(DST, KT, 0); FP8L_E() \
+  FP8L_M(2, 4) FP8L_RD(STN, 0, 0, 1); FP8L_E() \
+  FP8L_M(3, 4) FP8L_DMA1(DST, KT, 1); FP8L_E() \
+  FP8L_M(4, 4) FP8L_RD(STN, 0, 1, 0); FP8L_RD(STN, 1, 0, 0); FP8L_E() \
+  FP8L_M(5, 4) FP8L_RD(STN, 1, 0, 1); FP8L_DMA1(DST, KT, 2); FP8L_E() \
+  FP8L_M(6, 4) FP8L_RD(STN, 0, 1, 1); FP8L_E() \
+  FP8L_M(7, 4) FP8L_DMA1(DST, KT, 3); FP8L_E() \
+  FP8L_M(8, 4) FP8L_RD(STN, 0, 2, 0); FP8L_RD(STN, 1, 1, 0); FP8L_E() \
+  FP8L_M(9, 4) FP8L_RD(STN, 1, 1, 1); FP8L_DMA1(DST, KT, 4); FP8L_E() \
+  FP8L_M(10, 4) FP8L_RD(STN, 0, 2, 1); FP8L_E() \
+  FP8L_M(11, 4) FP8L_DMA1(DST, KT, 5); FP8L_E() \
+  FP8L_M(12, 4) FP8L_RD(STN, 0, 3, 0); FP8L_RD(STN, 1, 2, 0); FP8L_E() \
+  FP8L_M(13, 4) FP8L_RD(STN, 1, 2, 1); FP8L_DMA1(DST, KT, 6); FP8L_E() \
+  FP8L_M(14, 4) FP8L_RD(STN, 0, 3, 1); FP8L_E() \
+  FP8L_M(15, 4) FP8L_DMA1(DST, KT, 7); FP8L_E() \
+  FP8L_M(16, 4) FP8L_RD(STN, 1, 3, 0); FP8L_E() \
+  FP8L_M(17, 4) FP8L_RD(STN, 1, 3, 1); FP8L_DMA1(DST, KT, 8); FP8L_E() \
+  FP8L_M(18, 4) FP8L_E() \
+  FP8L_M(19, 4) FP8L_DMA1(DST, KT, 9); FP8L_E() \
+  FP8L_M(20, 4) FP8L_RD(STN, 1, 4, 0); FP8L_E() \
+  FP8L_M(21, 4) FP8L_RD(STN, 1, 4, 1); FP8L_DMA1(DST, KT, 10); FP8L_E() \
+  FP8L_M(22, 4) FP8L_E() \
+  FP8L_M(23, 4) FP8L_DMA1(DST, KT, 11); FP8L_E() \
+  FP8L_M(24, 4) FP8L_RD(STN, 1, 5, 0); FP8L_E() \
+  FP8L_M(25, 4) FP8L_RD(STN, 1, 5, 1); FP8L_DMA1(DST, KT, 12); FP8L_E() \
+  FP8L_M(26, 4) FP8L_E() \
+  FP8L_M(27, 4) FP8L_DMA1(DST, KT, 13); FP8L_E() \
+  FP8L_M(28, 4) FP8L_RD(STN, 1, 6, 0); FP8L_E() \
+  FP8L_M(29, 4) FP8L_RD(STN, 1, 6, 1); FP8L_DMA1(DST, KT, 14); FP8L_E() \
+  FP8L_M(30, 4) FP8L_E() \
+  FP8L_M(31, 4) FP8L_DMA1(DST, KT, 15); FP8L_E()
+#define FP8L_H2N(STN) \
+  FP8L_M(0, 4) FP8L_RD(STN, 0, 0, 0); FP8L_E() \
+  FP8L_M(1, 4) FP8L_E() \
+  FP8L_M(2, 4) FP8L_RD(STN, 0, 0, 1); FP8L_E() \
+  FP8L_M(3, 4) FP8L_E() \
+  FP8L_M(4, 4) FP8L_RD(STN, 0, 1, 0); FP8L_RD(STN, 1, 0, 0); FP8L_E() \
+  FP8L_M(5, 4) FP8L_RD(STN, 1, 0, 1); FP8L_E() \
+  FP8L_M(6, 4) FP8L_RD(STN, 0, 1, 1); FP8L_E() \
+  FP8L_M(7, 4) FP8L_E() \
+  FP8L_M(8, 4) FP8L_RD(STN, 0, 2, 0); FP8L_RD(STN, 1, 1, 0); FP8L_E() \
+  FP8L_M(9, 4) FP8L_RD(STN, 1, 1, 1); FP8L_E() \
+  FP8L_M(10, 4) FP8L_RD(STN, 0, 2, 1); FP8L_E() \
+  FP8L_M(11, 4) FP8L_E() \
+  FP8L_M(12, 4) FP8L_RD(STN, 0, 3, 0); FP8L_RD(STN, 1, 2, 0); FP8L_E() \
+  FP8L_M(13, 4) FP8L_RD(STN, 1, 2, 1); FP8L_E() \
+  FP8L_M(14, 4) FP8L_RD(STN, 0, 3, 1); FP8L_E() \
+  FP8L_M(15, 4) FP8L_E() \
+  FP8L_M(16, 4) FP8L_RD(STN, 1, 3, 0); FP8L_E() \
+  FP8L_M(17, 4) FP8L_RD(STN, 1, 3, 1); FP8L_E() \
+  FP8L_M(18, 4) FP8L_E() \
+  FP8L_M(19, 4) FP8L_E() \
+  FP8L_M(20, 4) FP8L_RD(STN, 1, 4, 0); FP8L_E() \
+  FP8L_M(21, 4) FP8L_RD(STN, 1, 4, 1); FP8L_E() \
+  FP8L_M(22, 4) FP8L_E() \
+  FP8L_M(23, 4) FP8L_E() \
+  FP8L_M(24, 4) FP8L_RD(STN, 1, 5, 0); FP8L_E() \
+  FP8L_M(25, 4) FP8L_RD(STN, 1, 5, 1); FP8L_E() \
+  FP8L_M(26, 4) FP8L_E() \
+  FP8L_M(27, 4) FP8L_E() \
+  FP8L_M(28, 4) FP8L_RD(STN, 1, 6, 0); FP8L_E() \
+  FP8L_M(29, 4) FP8L_RD(STN, 1, 6, 1); FP8L_E() \
+  FP8L_M(30, 4) FP8L_E() \
+  FP8L_M(31, 4) FP8L_E()
+#define FP8L_SYNC()                                                               \
+  wait_vmcnt0();                                                                  \
+  wait_lgkm0();                                                                   \
+  barrier_lds();
 
   const int nk = (K + BK - 1) / BK;
   if (nk > 0) {
-    FP8L_DMAALL(0, 0)
-    FP8L_DMAALL(1, 1)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) FP8L_DMA1(0, 0, q);
+    if (nk > 1) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) FP8L_DMA1(1, 1, q);
+    }
     wait_vmcnt0();
-    __builtin_amdgcn_s_barrier();
-    FP8L_READ0(0) FP8L_READ0(1) FP8L_READ0(2) FP8L_READ0(3)
-    FP8L_READ0(4) FP8L_READ0(5) FP8L_READ0(6) FP8L_READ0(7)
-    FP8L_READ0(8) FP8L_READ0(9) FP8L_READ0(10) FP8L_READ0(11)
-    FP8L_READ0(12) FP8L_READ0(13) FP8L_READ0(14) FP8L_READ0(15)
-    for (int t = 0; t < nk; ++t) {
+    barrier_lds();
+    // A0-3 and B0-6 of k-tile 0 (A4-7 and B7 are read in its first half)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) { FP8L_RD(0, 0, f, 0); FP8L_RD(0, 0, f, 1); }
+#pragma unroll
+    for (int f = 0; f < 7; ++f) { FP8L_RD(0, 1, f, 0); FP8L_RD(0, 1, f, 1); }
+    int t = 0;
+    // k-tiles with a DMA of k-tile t+2 into the stage just drained
+    for (; t + 2 < nk; ++t) {
       const int st = t & 1;
-      FP8L_SLOT0(0, st) FP8L_SLOT0(1, st) FP8L_SLOT0(2, st) FP8L_SLOT0(3, st)
-      FP8L_SLOT0(4, st) FP8L_SLOT0(5, st) FP8L_SLOT0(6, st) FP8L_SLOT0(7, st)
-      FP8L_SLOT0(8, st) FP8L_SLOT0(9, st) FP8L_SLOT0(10, st) FP8L_SLOT0(11, st)
-      FP8L_SLOT0(12, st) FP8L_SLOT0(13, st) FP8L_SLOT0(14, st) FP8L_SLOT0(15, st)
-      // this wave's DMA of k-tile t+1 landed and its reads of stage st are
-      // complete; after the barrier that holds for every wave: stage st^1 is
-      // readable and stage st can be refilled (past the end: with zeros, in
-      // a stage no later step reads)
-      wait_vmcnt0();
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
       const int stn = st ^ 1;
       const int kt2 = t + 2;
-      FP8L_SLOT1(0, st, stn, kt2) FP8L_SLOT1(1, st, stn, kt2)
-      FP8L_SLOT1(2, st, stn, kt2) FP8L_SLOT1(3, st, stn, kt2)
-      FP8L_SLOT1(4, st, stn, kt2) FP8L_SLOT1(5, st, stn, kt2)
-      FP8L_SLOT1(6, st, stn, kt2) FP8L_SLOT1(7, st, stn, kt2)
-      FP8L_SLOT1(8, st, stn, kt2) FP8L_SLOT1(9, st, stn, kt2)
-      FP8L_SLOT1(10, st, stn, kt2) FP8L_SLOT1(11, st, stn, kt2)
-      FP8L_SLOT1(12, st, stn, kt2) FP8L_SLOT1(13, st, stn, kt2)
-      FP8L_SLOT1(14, st, stn, kt2) FP8L_SLOT1(15, st, stn, kt2)
+      FP8L_H1(st)
+      FP8L_SYNC()
+      FP8L_H2(stn, st, kt2)
     }
-    wait_vmcnt0();   // no DMA may still target this workgroup's LDS
+    // the last one or two k-tiles: no DMA (the reads for k-tile nk fetch
+    // stale stage data into fragments that no MFMA uses)
+    for (; t < nk; ++t) {
+      const int st = t & 1;
+      const int stn = st ^ 1;
+      FP8L_H1(st)
+      FP8L_SYNC()
+      FP8L_H2N(stn)
+    }
   }
-#undef FP8L_READ0
-#undef FP8L_SLOT1
-#undef FP8L_SLOT0
-#undef FP8L_MFMA1
-#undef FP8L_READ1
-#undef FP8L_DMAALL
+#undef FP8L_SYNC
+#undef FP8L_H2N
+#undef FP8L_H2
+#undef FP8L_H1
+#undef FP8L_E
+#undef FP8L_M
+#undef FP8L_MF
+#undef FP8L_RD
 #undef FP8L_DMA1
 
   // ---- epilogue, staged through LDS: after one barrier every wave is done
@@ -282,53 +395,55 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
   // to its own region (rows padded to 272 bytes), then stores whole rows
   // with 16-byte chunks (16 lanes per 256-byte row).
   wait_lgkm0();
-  __builtin_amdgcn_s_barrier();
+  barrier_lds();
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   uint8_t *ep = lds + wave * EP_WAVE;
-  const float inv_a0 = a_vec ? 0.f : 1.0f / sa[0];
-  const float inv_b0 = b_vec ? 0.f : 1.0f / sb[0];
+  const float *inv = reinterpret_cast<const float *>(lds + INV_OFF);
+  const float inv_a0 = RW ? 0.f : 1.0f / sa[0];
+  const float inv_b0 = RW ? 0.f : 1.0f / sb[0];
+  // lane-derived values, recomputed here from an opaque copy of the thread
+  // index rather than kept live in registers across the main loop
+  int tid_e = tid;
+  asm volatile("" : "+v"(tid_e));
+  const int lane_e = tid_e & 63;
+  const int nq = (lane_e >> 4) * 4;     // first of the lane's 4 n in a block
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int ml = i * 32 + (lane & 31);               // row within the wave tile
-    const int m = m0 + wm * WM + ml;
-    const float inv_a = a_vec ? (m < M ? 1.0f / sa[m] : 0.f) : inv_a0;
+  for (int i = 0; i < NF; ++i) {
+    const int ml = i * FR + (lane_e & 15);              // row within the wave tile
+    const float inv_a = RW ? inv[wm * WM + ml] : inv_a0;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = j * 32 + g * 8 + kh * 4;         // col within the wave tile
-        const int n = n0 + wn * WN + nl;
-        float inv_b[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          inv_b[e] = b_vec ? (n + e < N ? 1.0f / sb[n + e] : 0.f) : inv_b0;
-        f32x2 v01 = {(acc[j][i][g * 4 + 0] * inv_a) * inv_b[0],
-                     (acc[j][i][g * 4 + 1] * inv_a) * inv_b[1]};
-        f32x2 v23 = {(acc[j][i][g * 4 + 2] * inv_a) * inv_b[2],
-                     (acc[j][i][g * 4 + 3] * inv_a) * inv_b[3]};
-        const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
-        const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
-        *reinterpret_cast<uint2 *>(ep + ml * EP_STRIDE + nl * 2) = make_uint2(p01, p23);
-      }
+    for (int j = 0; j < NF; ++j) {
+      const int nl = j * FR + nq;                       // col within the wave tile
+      v4f ib = {inv_b0, inv_b0, inv_b0, inv_b0};
+      if (RW) ib = *reinterpret_cast<const v4f *>(inv + BM + wn * WN + nl);
+      f32x2 v01 = {(acc[j][i][0] * inv_a) * ib[0], (acc[j][i][1] * inv_a) * ib[1]};
+      f32x2 v23 = {(acc[j][i][2] * inv_a) * ib[2], (acc[j][i][3] * inv_a) * ib[3]};
+      const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
+      const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
+      *reinterpret_cast<uint2 *>(ep + ml * EP_STRIDE + nl * 2) = make_uint2(p01, p23);
     }
   }
-  const int nbase = n0 + wn * WN;
-  const int mrow0 = m0 + wm * WM;
+  // store pass: 4 batches of 8 instructions; instruction u of batch it0
+  // covers tile rows (it0 + u) * 4 + lane / 16, 8 columns from (lane % 16) * 8
+  const int srow = m0 + wm * WM + (lane_e >> 4);
+  const int scol = n0 + wn * WN + (lane_e & 15) * 8;
+  const bool col_ok = scol < N;        // N % 16 == 0: all 8 columns or none
+  const int rows_left = M - srow;
+  const uint32_t soff0 = (uint32_t)((srow * N + scol) * 2);
+  const uint32_t row_step = (uint32_t)(8 * N);   // 4 rows of bf16
 #pragma unroll
   for (int it0 = 0; it0 < WM * WN * 2 / 16 / 64; it0 += 8) {
     v4u v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int id = (it0 + u) * 64 + lane;
+      const int id = (it0 + u) * 64 + lane_e;
       v[u] = *reinterpret_cast<const v4u *>(ep + (id >> 4) * EP_STRIDE + (id & 15) * 16);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int id = (it0 + u) * 64 + lane;
-      const int m = mrow0 + (id >> 4);
-      const int n = nbase + (id & 15) * 8;
-      const uint32_t off = (m < M && n < N) ? (uint32_t)((m * N + n) * 2) : OOB_C;
+      const bool ok = col_ok && (it0 + u) * 4 < rows_left;
+      const uint32_t off = ok ? soff0 + (uint32_t)(it0 + u) * row_step : OOB_C;
       __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off, 0, 0);
     }
   }
@@ -336,19 +451,18 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
 
 }  // namespace
 
-hipError_t gemm_launch(const uint8_t *A, const float *sa, int a_vec,
-                       const uint8_t *B, const float *sb, int b_vec, int64_t M,
-                       int64_t N, int64_t K, uint16_t *C, hipStream_t stream) {
+hipError_t gemm_launch(const uint8_t *A, const float *sa, const uint8_t *B,
+                       const float *sb, int rowwise, int64_t M, int64_t N,
+                       int64_t K, uint16_t *C, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
-  if (K % BK == 0)
-    hipLaunchKernelGGL(k_gemm_fp8_tn<true>, grid, dim3(THREADS), 0, stream, A, sa, a_vec, B,
-                       sb, b_vec, (int)M, (int)N, (int)K, C, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL(k_gemm_fp8_tn<false>, grid, dim3(THREADS), 0, stream, A, sa, a_vec, B,
-                       sb, b_vec, (int)M, (int)N, (int)K, C, tiles_m, tiles_n);
+  const bool kfull = K % BK == 0;
+  auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true> : k_gemm_fp8_tn<false, true>)
+                      : (kfull ? k_gemm_fp8_tn<true, false> : k_gemm_fp8_tn<false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(THREADS), 0, stream, A, sa, B, sb, (int)M, (int)N,
+                     (int)K, C, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
