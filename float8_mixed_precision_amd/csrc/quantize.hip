@@ -1,7 +1,13 @@
 // Dynamic-scaling quantization of a bf16 matrix to E4M3 on gfx950:
-//   1. k_amax_partial  : one read pass; per-tile maxima of |x| (tensorwise)
-//                        or per-tile row / column maxima (rowwise)
-//   2. k_finalize_*    : reduce the partials, s = 448 / max(amax, 1e-12)
+//   tensorwise:
+//   1. k_amax_tw       : one read pass, grid-stride; per-block maxima of |x|
+//   2. (in k_cast_transpose) every block reduces the partial maxima itself,
+//                        s = 448 / max(amax, 1e-12); block 0 stores s
+//                        (k_finalize_tw_empty does that alone for an empty x)
+//   rowwise:
+//   1. k_amax_partial  : one read pass; per-tile row / column maxima
+//   2. k_finalize_rowwise: reduce the partials, one scale per row / column
+//   both:
 //   3. k_cast_transpose: second read pass; writes q (row-major) directly and
 //                        qt (the transpose) through an LDS tile
 // The method is Float8 training of linear layers ("Torchtitan: A PyTorch
@@ -19,11 +25,19 @@
 namespace fp8l {
 namespace {
 
-// amax tile: 64 rows x 256 columns per 256-thread workgroup.  Each thread owns
-// one 8-column chunk (16 bytes of bf16) and walks 8 of the tile's rows.
+// rowwise amax tile: 64 rows x 256 columns per 256-thread workgroup.  Each
+// thread owns one 8-column chunk (16 bytes of bf16) and walks 8 of the
+// tile's rows.
 constexpr int AM_TR = 64;
 constexpr int AM_TC = 256;
 constexpr int AM_THREADS = 256;
+
+// tensorwise amax: chunks of 256 threads x 8 loads of 16 bytes (32 KB),
+// at most TW_MAX_BLOCKS workgroups in a grid-stride loop.  Workspace: one
+// u32 partial maximum per block.
+constexpr int TW_UNROLL = 8;
+constexpr int TW_CHUNK = AM_THREADS * TW_UNROLL;   // 16-byte vectors per chunk
+constexpr int TW_MAX_BLOCKS = 512;
 
 // cast tile: 128 rows x 128 columns per 256-thread workgroup.
 constexpr int CT_T = 128;
@@ -64,14 +78,86 @@ __device__ __forceinline__ U4 load16(const void *p) {
 
 // ----------------------------------------------------------------- amax --
 //
-// Tensorwise: part[tile] = max |x| over the tile (u16 bits).
-// Rowwise:    rowpart[tile_c][r] = max over the tile's columns of row r,
-//             colpart[tile_r][c] = max over the tile's rows of column c.
-template <bool ROWWISE>
+// Tensorwise.  Every load is issued unconditionally (index clamped into the
+// tensor, the value masked afterwards), so a thread's 8 loads are in flight
+// together.  Each block writes its maximum to part[block].
+__global__ __launch_bounds__(AM_THREADS) void k_amax_tw(
+    const uint4 *__restrict__ x, int64_t n16, uint32_t *__restrict__ part) {
+  const int tid = threadIdx.x;
+  uint32_t acc = 0;
+  const int64_t nchunks = (n16 + TW_CHUNK - 1) / TW_CHUNK;
+  for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
+    const int64_t base = ch * TW_CHUNK + tid;
+    uint4 v[TW_UNROLL];
+#pragma unroll
+    for (int u = 0; u < TW_UNROLL; ++u) {
+      const int64_t i = base + (int64_t)u * AM_THREADS;
+      v[u] = x[i < n16 ? i : n16 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < TW_UNROLL; ++u) {
+      const int64_t i = base + (int64_t)u * AM_THREADS;
+      const uint32_t keep = i < n16 ? 0x7FFF7FFFu : 0u;
+      acc = max_u16x2(acc, max_u16x2(max_u16x2(v[u].x & keep, v[u].y & keep),
+                                     max_u16x2(v[u].z & keep, v[u].w & keep)));
+    }
+  }
+  __shared__ uint32_t red[AM_THREADS / 64];
+  uint32_t m = wave_max(hmax16(acc));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t t = red[0];
+#pragma unroll
+    for (int w = 1; w < AM_THREADS / 64; ++w) t = max(t, red[w]);
+    part[blockIdx.x] = t;
+  }
+}
+
+// The tensor's amax from the nb partial maxima, by a whole 256-thread block
+// (all loads in flight together, index clamped and value masked); nb = 0 is
+// an empty tensor: amax 0.  Returns the u16 bits of |amax| to every thread.
+__device__ __forceinline__ uint32_t tw_amax_bits(const uint32_t *__restrict__ part, int nb,
+                                                 uint32_t *red) {
+  const int tid = threadIdx.x;
+  uint32_t t = 0;
+  if (nb > 0) {
+    uint32_t pv[TW_MAX_BLOCKS / AM_THREADS];
+#pragma unroll
+    for (int k = 0; k < TW_MAX_BLOCKS / AM_THREADS; ++k) {
+      const int i = tid + k * AM_THREADS;
+      pv[k] = part[i < nb ? i : nb - 1];
+    }
+#pragma unroll
+    for (int k = 0; k < TW_MAX_BLOCKS / AM_THREADS; ++k) t = max(t, pv[k]);
+  }
+  t = wave_max(t);
+  if ((tid & 63) == 0) red[tid >> 6] = t;
+  __syncthreads();
+  uint32_t mm = red[0];
+#pragma unroll
+  for (int w = 1; w < AM_THREADS / 64; ++w) mm = max(mm, red[w]);
+  return mm;
+}
+
+// Empty tensor: the scale of amax 0.
+__global__ __launch_bounds__(64) void k_finalize_tw_empty(float *scale, float *scale_t,
+                                                          float *amax_out) {
+  if (threadIdx.x == 0) {
+    const float sc = scale_from_amax(0.f);
+    scale[0] = sc;
+    scale_t[0] = sc;
+    if (amax_out) amax_out[0] = 0.f;
+  }
+}
+
+// Rowwise: rowpart[tile_c][r] = max over the tile's columns of row r,
+//          colpart[tile_r][c] = max over the tile's rows of column c.
+// Loads are unconditional (row clamped into the tensor, column chunk to 0)
+// and masked afterwards, so the 8 loads of a thread are in flight together.
 __global__ __launch_bounds__(AM_THREADS) void k_amax_partial(
     const uint16_t *__restrict__ x, int rows, int cols, int tiles_c,
-    uint16_t *__restrict__ part, uint16_t *__restrict__ rowpart,
-    uint16_t *__restrict__ colpart) {
+    uint16_t *__restrict__ rowpart, uint16_t *__restrict__ colpart) {
   const int tid = threadIdx.x;
   const int tile_c = blockIdx.x % tiles_c;
   const int tile_r = blockIdx.x / tiles_c;
@@ -80,83 +166,49 @@ __global__ __launch_bounds__(AM_THREADS) void k_amax_partial(
   const int r0 = tile_r * AM_TR;
   const int c = tile_c * AM_TC + cx * 8;
   const bool col_ok = c < cols;
+  const int cl = col_ok ? c : 0;
 
-  uint32_t acc = 0;               // tensorwise: packed max of |x| pairs
-  uint32_t cm[4] = {0, 0, 0, 0};  // rowwise: column maxima, 2 per dword
+  U4 v[AM_TR / 8];
 #pragma unroll
   for (int i = 0; i < AM_TR / 8; ++i) {
     const int r = r0 + ry + 8 * i;
-    U4 v = {0, 0, 0, 0};
-    if (col_ok && r < rows) v = load16(x + (size_t)r * cols + c);
-    v.x &= 0x7FFF7FFFu;
-    v.y &= 0x7FFF7FFFu;
-    v.z &= 0x7FFF7FFFu;
-    v.w &= 0x7FFF7FFFu;
-    if (!ROWWISE) {
-      acc = max_u16x2(acc, max_u16x2(max_u16x2(v.x, v.y), max_u16x2(v.z, v.w)));
-    } else {
-      cm[0] = max_u16x2(cm[0], v.x);
-      cm[1] = max_u16x2(cm[1], v.y);
-      cm[2] = max_u16x2(cm[2], v.z);
-      cm[3] = max_u16x2(cm[3], v.w);
-      uint32_t rm = hmax16(max_u16x2(max_u16x2(v.x, v.y), max_u16x2(v.z, v.w)));
-      rm = half_wave_max(rm);      // the 32 lanes of a half-wave share row r
-      if (cx == 0 && r < rows) rowpart[(size_t)tile_c * rows + r] = (uint16_t)rm;
-    }
+    v[i] = load16(x + (size_t)min(r, rows - 1) * cols + cl);
+  }
+  uint32_t cm[4] = {0, 0, 0, 0};  // column maxima, 2 per dword
+#pragma unroll
+  for (int i = 0; i < AM_TR / 8; ++i) {
+    const int r = r0 + ry + 8 * i;
+    const uint32_t keep = (col_ok && r < rows) ? 0x7FFF7FFFu : 0u;
+    const uint32_t x0 = v[i].x & keep, x1 = v[i].y & keep;
+    const uint32_t x2 = v[i].z & keep, x3 = v[i].w & keep;
+    cm[0] = max_u16x2(cm[0], x0);
+    cm[1] = max_u16x2(cm[1], x1);
+    cm[2] = max_u16x2(cm[2], x2);
+    cm[3] = max_u16x2(cm[3], x3);
+    uint32_t rm = hmax16(max_u16x2(max_u16x2(x0, x1), max_u16x2(x2, x3)));
+    rm = half_wave_max(rm);        // the 32 lanes of a half-wave share row r
+    if (cx == 0 && r < rows) rowpart[(size_t)tile_c * rows + r] = (uint16_t)rm;
   }
 
-  if (!ROWWISE) {
-    __shared__ uint32_t red[AM_THREADS / 64];
-    uint32_t m = wave_max(hmax16(acc));
-    if ((tid & 63) == 0) red[tid >> 6] = m;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t t = red[0];
+  // reduce the column maxima over the 8 row phases through LDS
+  __shared__ uint32_t cred[8][AM_TC / 2];
 #pragma unroll
-      for (int w = 1; w < AM_THREADS / 64; ++w) t = max(t, red[w]);
-      part[blockIdx.x] = (uint16_t)t;
-    }
-  } else {
-    // reduce the column maxima over the 8 row phases through LDS
-    __shared__ uint32_t cred[8][AM_TC / 2];
+  for (int j = 0; j < 4; ++j) cred[ry][cx * 4 + j] = cm[j];
+  __syncthreads();
+  if (tid < AM_TC / 2) {
+    uint32_t t = cred[0][tid];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cred[ry][cx * 4 + j] = cm[j];
-    __syncthreads();
-    if (tid < AM_TC / 2) {
-      uint32_t t = cred[0][tid];
-#pragma unroll
-      for (int p = 1; p < 8; ++p) t = max_u16x2(t, cred[p][tid]);
-      const int cc = tile_c * AM_TC + tid * 2;
-      if (cc < cols) {
-        uint16_t *dst = colpart + (size_t)tile_r * cols + cc;
-        dst[0] = (uint16_t)(t & 0xFFFFu);
-        dst[1] = (uint16_t)(t >> 16);
-      }
+    for (int p = 1; p < 8; ++p) t = max_u16x2(t, cred[p][tid]);
+    const int cc = tile_c * AM_TC + tid * 2;
+    if (cc < cols) {
+      uint16_t *dst = colpart + (size_t)tile_r * cols + cc;
+      dst[0] = (uint16_t)(t & 0xFFFFu);
+      dst[1] = (uint16_t)(t >> 16);
     }
   }
 }
 
 // ------------------------------------------------------------- finalize --
-
-__global__ __launch_bounds__(1024) void k_finalize_tensorwise(
-    const uint16_t *__restrict__ part, int nparts, float *scale,
-    float *scale_t, float *amax_out) {
-  __shared__ uint32_t red[1024 / 64];
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, (uint32_t)part[i]);
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t t = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t = max(t, red[w]);
-    const float a = bf16_to_f32(t);
-    const float s = scale_from_amax(a);
-    scale[0] = s;
-    scale_t[0] = s;
-    if (amax_out) amax_out[0] = a;
-  }
-}
 
 // one thread per output: rows first (max over tiles_c partials), then columns
 __global__ __launch_bounds__(256) void k_finalize_rowwise(
@@ -196,10 +248,15 @@ __global__ __launch_bounds__(256) void k_finalize_rowwise(
 //
 // Phase B: each thread reads 16-byte chunks (16 rows of one column) from LDS
 // and stores them to qt: eight threads write one 128-byte qt row segment.
+//
+// Tensorwise: the block first reduces the amax pass's partial maxima to the
+// tensor's scale; block 0 also stores it (scale, scale_t, amax_out).
+// Rowwise: scale / scale_t are inputs (from k_finalize_rowwise).
 template <bool ROWWISE>
 __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
     const uint16_t *__restrict__ x, int rows, int cols, int tiles_c,
-    const float *__restrict__ scale, const float *__restrict__ scale_t,
+    float *__restrict__ scale, float *__restrict__ scale_t,
+    const uint32_t *__restrict__ part, int nparts, float *__restrict__ amax_out,
     uint8_t *__restrict__ q, uint8_t *__restrict__ qt) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[CT_T * CT_T];
   const int tid = threadIdx.x;
@@ -218,7 +275,15 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
 #pragma unroll
     for (int j = 0; j < 8; ++j) sc[j] = col_ok ? scale_t[c + j] : 0.f;
   } else {
-    s_t = scale[0];
+    __shared__ uint32_t red[CT_THREADS / 64];
+    const uint32_t am = tw_amax_bits(part, nparts, red);
+    const float a = bf16_to_f32(am);
+    s_t = scale_from_amax(a);
+    if (blockIdx.x == 0 && tid == 0) {
+      scale[0] = s_t;
+      scale_t[0] = s_t;
+      if (amax_out) amax_out[0] = a;
+    }
   }
 
 #pragma unroll
@@ -315,15 +380,21 @@ AmaxGeom amax_geom(int64_t rows, int64_t cols) {
   return {cdiv(rows, AM_TR), cdiv(cols, AM_TC)};
 }
 
+int64_t tw_blocks(int64_t rows, int64_t cols) {
+  const int64_t nchunks = cdiv(rows * cols / 8, TW_CHUNK);
+  return nchunks < TW_MAX_BLOCKS ? nchunks : TW_MAX_BLOCKS;
+}
+
 }  // namespace
 
 size_t quantize_workspace_bytes(int64_t rows, int64_t cols, int scaling) {
   const AmaxGeom g = amax_geom(rows, cols);
   size_t bytes;
-  if (scaling == FP8L_TENSORWISE)
-    bytes = (size_t)(g.tiles_r * g.tiles_c) * sizeof(uint16_t);
-  else
+  if (scaling == FP8L_TENSORWISE) {
+    bytes = (size_t)tw_blocks(rows, cols) * sizeof(uint32_t);
+  } else {
     bytes = (size_t)(g.tiles_c * rows + g.tiles_r * cols) * sizeof(uint16_t) + 256;
+  }
   return (bytes + 255) & ~(size_t)255;
 }
 
@@ -336,20 +407,23 @@ hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
   const uint16_t *xb = static_cast<const uint16_t *>(x);
   uint16_t *ws = static_cast<uint16_t *>(workspace);
   const int R = (int)rows, C = (int)cols;
+  const int64_t nb = scaling == FP8L_TENSORWISE ? tw_blocks(rows, cols) : 0;
+  uint32_t *part = static_cast<uint32_t *>(workspace);
   if (scaling == FP8L_TENSORWISE) {
-    if (ntiles > 0)
-      hipLaunchKernelGGL(k_amax_partial<false>, dim3((unsigned)ntiles), dim3(AM_THREADS), 0,
-                         stream, xb, R, C, (int)g.tiles_c, ws, nullptr, nullptr);
-    hipLaunchKernelGGL(k_finalize_tensorwise, dim3(1), dim3(1024), 0, stream, ws,
-                       (int)ntiles, scale, scale_t, amax_out);
+    if (nb > 0)
+      hipLaunchKernelGGL(k_amax_tw, dim3((unsigned)nb), dim3(AM_THREADS), 0, stream,
+                         static_cast<const uint4 *>(x), rows * cols / 8, part);
+    else
+      hipLaunchKernelGGL(k_finalize_tw_empty, dim3(1), dim3(64), 0, stream, scale, scale_t,
+                         amax_out);
   } else {
     uint16_t *rowpart = ws;
     // column partials start on a 256-byte boundary after the row partials
     size_t off = ((size_t)(g.tiles_c * rows) * sizeof(uint16_t) + 255) & ~(size_t)255;
     uint16_t *colpart = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(workspace) + off);
     if (ntiles > 0)
-      hipLaunchKernelGGL(k_amax_partial<true>, dim3((unsigned)ntiles), dim3(AM_THREADS), 0,
-                         stream, xb, R, C, (int)g.tiles_c, nullptr, rowpart, colpart);
+      hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)ntiles), dim3(AM_THREADS), 0,
+                         stream, xb, R, C, (int)g.tiles_c, rowpart, colpart);
     if (rows + cols > 0)
       hipLaunchKernelGGL(k_finalize_rowwise, dim3((unsigned)cdiv(rows + cols, 256)), dim3(256),
                          0, stream, rowpart, colpart, R, C, (int)g.tiles_c, (int)g.tiles_r,
@@ -362,11 +436,13 @@ hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
     if (scaling == FP8L_TENSORWISE)
       hipLaunchKernelGGL(k_cast_transpose<false>, dim3((unsigned)(ct_r * ct_c)),
                          dim3(CT_THREADS), 0, stream, xb, R, C, (int)ct_c, scale, scale_t,
-                         static_cast<uint8_t *>(q), static_cast<uint8_t *>(qt));
+                         part, (int)nb, amax_out, static_cast<uint8_t *>(q),
+                         static_cast<uint8_t *>(qt));
     else
       hipLaunchKernelGGL(k_cast_transpose<true>, dim3((unsigned)(ct_r * ct_c)),
                          dim3(CT_THREADS), 0, stream, xb, R, C, (int)ct_c, scale, scale_t,
-                         static_cast<uint8_t *>(q), static_cast<uint8_t *>(qt));
+                         nullptr, 0, nullptr, static_cast<uint8_t *>(q),
+                         static_cast<uint8_t *>(qt));
   }
   return hipGetLastError();
 }

@@ -111,7 +111,8 @@ def alloc_quantized(rows: int, cols: int, rowwise: bool, device) -> Quantized:
 
 
 def alloc_workspace(rows: int, cols: int, rowwise: bool, device) -> torch.Tensor:
-    return torch.empty(max(fp8_linear_workspace_bytes(rows, cols, rowwise), 256),
+    """Zero-filled, as fp8_linear_quantize requires of a new workspace."""
+    return torch.zeros(max(fp8_linear_workspace_bytes(rows, cols, rowwise), 256),
                        dtype=torch.uint8, device=device)
 
 
@@ -202,7 +203,7 @@ class LinearStep:
         ws = max(fp8_linear_workspace_bytes(self.M, self.K, rowwise),
                  fp8_linear_workspace_bytes(self.N, self.K, rowwise),
                  fp8_linear_workspace_bytes(self.M, self.N, rowwise), 256)
-        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(ws, dtype=torch.uint8, device=dev)
         self.out = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
         self.grad_x = torch.empty((self.M, self.K), dtype=torch.bfloat16, device=dev)
         self.grad_w = torch.empty((self.N, self.K), dtype=torch.bfloat16, device=dev)

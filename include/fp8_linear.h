@@ -75,8 +75,8 @@ extern "C" {
 
 /*
  * Bytes of device workspace fp8_linear_quantize needs for an x of
- * [rows, cols] with the given scaling (partial maxima of the amax pass).
- * Returns 0 for invalid arguments.
+ * [rows, cols] with the given scaling (partial maxima of the amax pass;
+ * 0 for an empty tensorwise x).  Returns 0 for invalid arguments.
  */
 FP8L_API size_t fp8_linear_workspace_bytes(int64_t rows, int64_t cols, int scaling);
 

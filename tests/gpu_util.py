@@ -38,9 +38,9 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def gpu_quantize(bits: np.ndarray, rowwise: bool):
+def gpu_quantize(bits: np.ndarray, rowwise: bool, workspace=None):
     x = dev_bf16(bits)
-    qz = ops.fp8_linear_quantize(x, rowwise)
+    qz = ops.fp8_linear_quantize(x, rowwise, workspace=workspace)
     torch.cuda.synchronize()
     return host(qz.q), host(qz.qt), host(qz.scale), host(qz.scale_t), host(qz.amax)
 

@@ -157,6 +157,21 @@ def test_quantize_empty(shape, rowwise):
         assert G.host(qz.scale)[0] == s_empty and G.host(qz.amax)[0] == 0
 
 
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+def test_quantize_workspace_reuse(rowwise):
+    """One workspace serves calls of different sizes in a row (stale partial
+    maxima of a bigger earlier call must not leak into a smaller one), and
+    each result is bit-exact."""
+    shapes = [(1040, 4112), (272, 400), (2064, 2064), (16, 16), (1040, 4112)]
+    need = max(ops.fp8_linear_workspace_bytes(r, c, rowwise) for r, c in shapes)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=G.DEV)   # large stale maxima
+    for k, shape in enumerate(shapes):
+        x = W.random_bf16(30 + k, shape, 1.0, 5)
+        G.say("quantize workspace reuse", shape, "rowwise", rowwise)
+        G.assert_quantize_equal(G.gpu_quantize(x, rowwise, workspace=ws),
+                                oracle.quantize(x, rowwise), "%s call %d" % (shape, k))
+
+
 def test_quantize_scaled_max_maps_to_448():
     """Invariant on the device: the element(s) holding the amax encode to
     +-448 (0x7E / 0xFE)."""
