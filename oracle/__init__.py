@@ -70,6 +70,13 @@ class Oracle:
                                     i64, i64, i64, P, P]
         lib.orc_gemm_tn_sampled.argtypes = [P, P, ctypes.c_int, P, P,
                                             ctypes.c_int, i64, P, P, i64, P, P]
+        lib.orc_amax.restype = ctypes.c_float
+        lib.orc_amax.argtypes = [P, i64]
+        lib.orc_quantize_scaled.argtypes = [P, i64, i64, ctypes.c_float, P, P]
+        lib.orc_gemm_tn_f32.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int,
+                                        i64, i64, i64, P]
+        lib.orc_gemm_tn_f32_sampled.argtypes = [P, P, ctypes.c_int, P, P,
+                                                ctypes.c_int, i64, P, P, i64, P]
         self.lib = lib
         self.path = lib_path
 
@@ -136,6 +143,22 @@ class Oracle:
                               _ptr(qt), _ptr(s), _ptr(st), _ptr(am))
         return q, qt, s, st, am
 
+    def amax(self, x_bits) -> np.float32:
+        """max |x| over a bf16 tensor (NaN-propagating; 0 for an empty one)."""
+        x = _c(x_bits, np.uint16)
+        return np.float32(self.lib.orc_amax(_ptr(x), x.size))
+
+    def quantize_scaled(self, x_bits, scale):
+        """Cast with a caller-given tensorwise multiplier s:
+        q = enc(fl32(x * s)) [rows, cols], qt its transpose [cols, rows]."""
+        x = _c(x_bits, np.uint16)
+        rows, cols = x.shape
+        q = np.empty((rows, cols), dtype=np.uint8)
+        qt = np.empty((cols, rows), dtype=np.uint8)
+        self.lib.orc_quantize_scaled(_ptr(x), rows, cols, float(np.float32(scale)),
+                                     _ptr(q), _ptr(qt))
+        return q, qt
+
     # -------------------------------------------------------------- GEMM --
 
     def gemm_tn(self, a, sa, b, sb, return_acc: bool = False):
@@ -181,6 +204,43 @@ class Oracle:
                                      _ptr(ii), _ptr(jj), ii.size, _ptr(out),
                                      _ptr(acc))
         return (out, acc) if return_acc else out
+
+    def gemm_tn_f32(self, a, sa, b, sb):
+        """fp32 form of gemm_tn: fl32(fl32(acc * (1/sa_i)) * (1/sb_j)), no
+        bf16 rounding.  Returns float32 [m, n]."""
+        a = _c(a, np.uint8)
+        b = _c(b, np.uint8)
+        sa = _c(np.atleast_1d(sa), np.float32)
+        sb = _c(np.atleast_1d(sb), np.float32)
+        m, k = a.shape
+        n, k2 = b.shape
+        assert k == k2
+        assert sa.size in (1, m) and sb.size in (1, n)
+        out = np.empty((m, n), dtype=np.float32)
+        self.lib.orc_gemm_tn_f32(_ptr(a), _ptr(sa), int(sa.size != 1), _ptr(b),
+                                 _ptr(sb), int(sb.size != 1), m, n, k, _ptr(out))
+        return out
+
+    def gemm_tn_f32_sampled(self, a, sa, b, sb, ii, jj):
+        """gemm_tn_f32 evaluated only at (ii[s], jj[s])."""
+        a = _c(a, np.uint8)
+        b = _c(b, np.uint8)
+        sa = _c(np.atleast_1d(sa), np.float32)
+        sb = _c(np.atleast_1d(sb), np.float32)
+        ii = _c(ii, np.int64)
+        jj = _c(jj, np.int64)
+        m, k = a.shape
+        n, k2 = b.shape
+        assert k == k2 and ii.shape == jj.shape
+        assert sa.size in (1, m) and sb.size in (1, n)
+        if ii.size:
+            assert ii.min() >= 0 and ii.max() < m
+            assert jj.min() >= 0 and jj.max() < n
+        out = np.empty(ii.shape, dtype=np.float32)
+        self.lib.orc_gemm_tn_f32_sampled(_ptr(a), _ptr(sa), int(sa.size != 1),
+                                         _ptr(b), _ptr(sb), int(sb.size != 1), k,
+                                         _ptr(ii), _ptr(jj), ii.size, _ptr(out))
+        return out
 
 
 _default = None
@@ -228,6 +288,22 @@ def gemm_tn(a, sa, b, sb, return_acc=False):
 
 def gemm_tn_sampled(a, sa, b, sb, ii, jj, return_acc=False):
     return default().gemm_tn_sampled(a, sa, b, sb, ii, jj, return_acc)
+
+
+def amax(x_bits):
+    return default().amax(x_bits)
+
+
+def quantize_scaled(x_bits, scale):
+    return default().quantize_scaled(x_bits, scale)
+
+
+def gemm_tn_f32(a, sa, b, sb):
+    return default().gemm_tn_f32(a, sa, b, sb)
+
+
+def gemm_tn_f32_sampled(a, sa, b, sb, ii, jj):
+    return default().gemm_tn_f32_sampled(a, sa, b, sb, ii, jj)
 
 
 # ------------------------------------------------------- parity metrics --

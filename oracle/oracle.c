@@ -224,6 +224,34 @@ void orc_quantize(const uint16_t *x, int64_t rows, int64_t cols, int rowwise,
     }
 }
 
+/* max |x| over a bf16 tensor of n elements (NaN-propagating; 0 when empty):
+ * one rank's share of the global tensorwise amax. */
+float orc_amax(const uint16_t *x, int64_t n)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; i++)
+        a = amax_update(a, orc_bf16_to_f32(x[i]));
+    return a;
+}
+
+/* Cast with a scale given by the caller (one tensorwise multiplier s, e.g.
+ * from a global amax): q[r][c] = enc(fl32(x[r][c] * s)) and qt[c][r] = the
+ * same code.  With s = scale_from_amax(amax(x)) this is the tensorwise
+ * quantize above. */
+void orc_quantize_scaled(const uint16_t *x, int64_t rows, int64_t cols, float s,
+                         uint8_t *q, uint8_t *qt)
+{
+    tables_init();
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++) {
+            float y = orc_bf16_to_f32(x[r * cols + c]) * s;
+            uint8_t code = orc_e4m3_encode(y);
+            q[r * cols + c] = code;
+            qt[c * rows + r] = code;
+        }
+}
+
 /* ---------------------------------------------------------------- GEMM -- */
 
 /* One output element of a scaled fp8 GEMM with both operands contiguous
@@ -232,8 +260,8 @@ void orc_quantize(const uint16_t *x, int64_t rows, int64_t cols, int rowwise,
  *   out = bf16( fl32( fl32(acc * (1/sa)) * (1/sb) ) )
  * Every fp8 x fp8 product is exact in fp32, so the only roundings are the
  * k additions, the two reciprocals, the two scalings and the final bf16. */
-static uint16_t gemm_element(const uint8_t *arow, const uint8_t *brow,
-                             int64_t k, float sa, float sb, float *acc_out)
+static float gemm_element_f32(const uint8_t *arow, const uint8_t *brow,
+                              int64_t k, float sa, float sb, float *acc_out)
 {
     float acc = 0.0f;
     for (int64_t t = 0; t < k; t++)
@@ -242,8 +270,13 @@ static uint16_t gemm_element(const uint8_t *arow, const uint8_t *brow,
     float inv_a = 1.0f / sa;
     float inv_b = 1.0f / sb;
     float v = acc * inv_a;
-    v = v * inv_b;
-    return orc_f32_to_bf16(v);
+    return v * inv_b;
+}
+
+static uint16_t gemm_element(const uint8_t *arow, const uint8_t *brow,
+                             int64_t k, float sa, float sb, float *acc_out)
+{
+    return orc_f32_to_bf16(gemm_element_f32(arow, brow, k, sa, sb, acc_out));
 }
 
 /* Full GEMM: out[i][j] (row-major, m x n) from a[m][k] and b[n][k].
@@ -276,5 +309,35 @@ void orc_gemm_tn_sampled(const uint8_t *a, const float *sa, int a_vec,
         out[s] = gemm_element(a + i * k, b + j * k, k,
                               a_vec ? sa[i] : sa[0], b_vec ? sb[j] : sb[0],
                               acc ? &acc[s] : 0);
+    }
+}
+
+/* The fp32-output form of the same GEMM (the value before the final bf16
+ * rounding), as a grad_W that is reduce-scattered in fp32 would need:
+ *   out[i][j] = fl32( fl32(acc * (1/sa)) * (1/sb) )                         */
+void orc_gemm_tn_f32(const uint8_t *a, const float *sa, int a_vec,
+                     const uint8_t *b, const float *sb, int b_vec,
+                     int64_t m, int64_t n, int64_t k, float *out)
+{
+    tables_init();
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; i++)
+        for (int64_t j = 0; j < n; j++)
+            out[i * n + j] = gemm_element_f32(a + i * k, b + j * k, k,
+                                              a_vec ? sa[i] : sa[0],
+                                              b_vec ? sb[j] : sb[0], 0);
+}
+
+void orc_gemm_tn_f32_sampled(const uint8_t *a, const float *sa, int a_vec,
+                             const uint8_t *b, const float *sb, int b_vec,
+                             int64_t k, const int64_t *ii, const int64_t *jj,
+                             int64_t ns, float *out)
+{
+    tables_init();
+    #pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t s = 0; s < ns; s++) {
+        int64_t i = ii[s], j = jj[s];
+        out[s] = gemm_element_f32(a + i * k, b + j * k, k,
+                                  a_vec ? sa[i] : sa[0], b_vec ? sb[j] : sb[0], 0);
     }
 }

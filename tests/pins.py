@@ -401,8 +401,74 @@ def check_gemm_sampled(o, seed: int = 12) -> None:
     assert np.array_equal(o.gemm_tn_sampled(a, sa, b, sb, ii, jj), full[ii, jj])
 
 
+def check_amax(o, seed: int = 13) -> None:
+    """max |x| of a bf16 tensor against numpy on torch's bf16 decode: NaN
+    propagates, the empty tensor gives 0, and it is the tensorwise quantize's
+    amax."""
+    from float8_mixed_precision_amd.workloads import random_bf16
+    rng = np.random.default_rng(seed)
+    for shp in ((64, 48), (7, 16), (1, 16)):
+        xb = random_bf16(seed, shp, float(rng.uniform(0.01, 100)), 0)
+        f = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).float().numpy()
+        assert np.float32(o.amax(xb)) == np.float32(np.abs(f).max())
+        assert _bits(np.atleast_1d(o.amax(xb))) == _bits(o.quantize(xb, False)[4])
+        xn = xb.copy()
+        xn[shp[0] // 2, 3] = 0x7FC0
+        assert np.isnan(o.amax(xn))
+        for pos in ((0, 0), (shp[0] - 1, shp[1] - 1)):     # the first and the last element
+            xe = xb.copy()
+            xe[pos] = 0xC7C8                                  # -102400, the unique maximum |x|
+            assert o.amax(xe) == np.float32(102400.0), "amax misses element %s" % (pos,)
+    assert o.amax(np.zeros((0, 16), np.uint16)) == 0.0
+
+
+def check_quantize_scaled(o, seed: int = 14) -> None:
+    """Cast with a given scale against torch's saturating encode of the fp32
+    product (numpy float32 multiply), over scales that keep, shrink and
+    saturate the values; qt is q transposed; with the tensor's own scale it
+    is the tensorwise quantize."""
+    from float8_mixed_precision_amd.workloads import random_bf16
+    for si, shp in enumerate(((64, 48), (37, 16), (128, 80))):
+        xb = random_bf16(seed, shp, 1.0, si)
+        f = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).float().numpy()
+        for s in (1.0, 3.7e-3, 55.0, 1e5, float(o.scale_from_amax(o.amax(xb)))):
+            q, qt = o.quantize_scaled(xb, s)
+            want = torch_encode_sat(f * np.float32(s))
+            assert np.array_equal(q, want), "quantize_scaled q, scale %g" % s
+            assert np.array_equal(qt, q.T)
+        q0, qt0 = o.quantize(xb, False)[:2]
+        q1, qt1 = o.quantize_scaled(xb, o.scale_from_amax(o.amax(xb)))
+        assert np.array_equal(q0, q1) and np.array_equal(qt0, qt1)
+
+
+def check_gemm_f32(o, seed: int = 15) -> None:
+    """The fp32-output GEMM is the bf16 GEMM before its last rounding: its
+    bf16 rounding (by torch) equals gemm_tn bit for bit, and with sums that
+    are exact and power-of-two scales it equals exact / (sa * sb) exactly."""
+    tv = torch_e4m3_values()
+    rng = np.random.default_rng(seed)
+    m, n, k = 33, 47, 200
+    a = random_codes(rng, (m, k))
+    b = random_codes(rng, (n, k))
+    sa = (10.0 ** rng.uniform(-2, 4, m)).astype(np.float32)
+    sb = (10.0 ** rng.uniform(-2, 4, n)).astype(np.float32)
+    f = o.gemm_tn_f32(a, sa, b, sb)
+    assert np.array_equal(torch_bf16_bits(f), o.gemm_tn(a, sa, b, sb))
+    ii = rng.integers(0, m, 300)
+    jj = rng.integers(0, n, 300)
+    assert np.array_equal(_bits(o.gemm_tn_f32_sampled(a, sa, b, sb, ii, jj)), _bits(f[ii, jj]))
+    m, n, k = 12, 20, 64
+    a = random_codes(rng, (m, k), 0x38, 0x57)
+    b = random_codes(rng, (n, k), 0x38, 0x57)
+    sa = (2.0 ** rng.integers(-4, 5, m)).astype(np.float32)
+    sb = (2.0 ** rng.integers(-4, 5, n)).astype(np.float32)
+    ex = _exact_sum(a, b, tv) / (sa[:, None].astype(np.float64) * sb[None, :])
+    assert np.array_equal(o.gemm_tn_f32(a, sa, b, sb).astype(np.float64), ex)
+
+
 ALL_CHECKS = [check_decode, check_encode_random, check_encode_brute_force,
               check_encode_invariants, check_bf16, check_scale,
               check_quantize_vs_library, check_quantize_invariants,
               check_gemm_vs_exact, check_gemm_exact_cases, check_gemm_scales,
-              check_gemm_tiny_brute_force, check_gemm_sampled]
+              check_gemm_tiny_brute_force, check_gemm_sampled, check_amax,
+              check_quantize_scaled, check_gemm_f32]

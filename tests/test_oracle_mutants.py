@@ -40,6 +40,17 @@ MUTANTS = {
     "epilogue_scale": ("float inv_b = 1.0f / sb;", "float inv_b = 1.0f / sa;"),
     # epilogue: bf16 rounding truncates
     "bf16_truncate": ("if (dd < du) return down;", "if (1) return down;"),
+    # shard amax: first element skipped
+    "amax_skip_first": ("for (int64_t i = 0; i < n; i++)\n        a = amax_update(",
+                        "for (int64_t i = 1; i < n; i++)\n        a = amax_update("),
+    # cast with a given scale: the scale is dropped
+    "scaled_no_scale": ("float y = orc_bf16_to_f32(x[r * cols + c]) * s;",
+                        "float y = orc_bf16_to_f32(x[r * cols + c]);"),
+    # cast with a given scale: qt rows reversed
+    "scaled_qt_index": ("            qt[c * rows + r] = code;\n        }\n}\n\n/* ----",
+                        "            qt[c * rows + (rows - 1 - r)] = code;\n        }\n}\n\n/* ----"),
+    # fp32 GEMM: output stored transposed
+    "gemm_f32_store": ("out[i * n + j] = gemm_element_f32(", "out[j * m + i] = gemm_element_f32("),
 }
 
 
