@@ -123,6 +123,62 @@ def cpu_baseline(wl, rows_g: int, rows_q: int = 512):
                       "%.1f s per step" % (rows_q, rows_g, flops_sampled / 1e9, wall, est)}
 
 
+def measure_next_rows(steps, stream, reps: int = 5):
+    """The entry points beyond the linear's own step, timed on the same FFN
+    tensors after the main measurement (outside `value`): the shard amax and
+    the cast with a given scale of Float8 all-gather, and grad_W with an
+    fp32 output.  HIP events on the launch stream around every call."""
+    import torch
+    from float8_mixed_precision_amd import ops
+
+    biggest = max(ls.N * ls.K for ls in steps)
+    gw32 = torch.empty(biggest, dtype=torch.float32, device=steps[0].x.device)
+    amax_out = torch.empty(1, dtype=torch.float32, device=steps[0].x.device)
+    rec = {"amax": [], "quantize_scaled": [], "bwd_w_f32": []}
+
+    def timed(kind, work, fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        rec[kind].append((work, e0, e1))
+
+    for r in range(reps + 1):
+        for ls in steps:
+            for t, qz in ((ls.x, ls.qx), (ls.w, ls.qw), (ls.dy, ls.qdy)):
+                n = t.numel()
+                timed("amax", 2 * n, lambda: ops.fp8_linear_amax(t, amax_out, ls.ws))
+                timed("quantize_scaled", 4 * n,
+                      lambda: ops.fp8_linear_quantize_scaled(t, qz.scale, qz.q, qz.qt))
+            g = gw32[:ls.N * ls.K].view(ls.N, ls.K)
+            timed("bwd_w_f32", 2 * ls.M * ls.N * ls.K,
+                  lambda: ops.fp8_linear_bwd_w_f32(ls.qdy.qt, ls.qdy.scale_t, ls.qx.qt,
+                                                   ls.qx.scale_t, ls.M, ls.N, ls.K,
+                                                   ls.rowwise, g))
+        if r == 0:                      # first round is warm-up
+            torch.cuda.synchronize()
+            for v in rec.values():
+                v.clear()
+    torch.cuda.synchronize()
+    out = {}
+    for kind, v in rec.items():
+        work = sum(w for w, _, _ in v)
+        ms = sum(a.elapsed_time(b) for _, a, b in v)
+        if kind == "bwd_w_f32":
+            ach = work / (ms * 1e-3) / 1e12
+            out[kind] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4),
+                         "calls": len(v), "avg_call_us": round(ms * 1e3 / len(v), 2)}
+        else:
+            ach = work / (ms * 1e-3) / 1e9
+            out[kind] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                         "bytes_per_element": 2 if kind == "amax" else 4,
+                         "calls": len(v), "avg_call_us": round(ms * 1e3 / len(v), 2)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -249,6 +305,8 @@ def main():
                                    "quantize": round(q_ms / args.steps, 4)},
         "cpu_baseline": None,
     }
+    print("[bench] next rows", file=sys.stderr, flush=True)
+    result["next_rows"] = measure_next_rows(steps, stream)
     del steps, shared
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -115,6 +115,50 @@ int fp8_linear_bwd(const void *dyq, const float *sdy, const void *dytq,
   return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
 }
 
+int fp8_linear_amax(const void *x, int64_t rows, int64_t cols, float *amax_out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  if (bad_dim(rows) || bad_dim(cols) || rows * cols > kMaxElems) return FP8L_ESHAPE;
+  if (!amax_out || (rows * cols > 0 && !x)) return FP8L_EINVAL;
+  const size_t need = fp8l::quantize_workspace_bytes(rows, cols, FP8L_TENSORWISE);
+  if (need > 0 && !workspace) return FP8L_EINVAL;
+  if (workspace_bytes < need) return FP8L_EWORKSPACE;
+  if (misaligned(x) || misaligned(workspace) || (reinterpret_cast<uintptr_t>(amax_out) & 3u))
+    return FP8L_EALIGN;
+  hipError_t e = fp8l::amax_launch(x, rows, cols, amax_out, workspace,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
+int fp8_linear_quantize_scaled(const void *x, int64_t rows, int64_t cols, const float *scale,
+                               void *q, void *qt, void *stream) {
+  if (bad_dim(rows) || bad_dim(cols) || rows * cols > kMaxElems) return FP8L_ESHAPE;
+  if (rows * cols == 0) return FP8L_OK;
+  if (!x || !scale || !q || !qt) return FP8L_EINVAL;
+  if (misaligned(x) || misaligned(q) || misaligned(qt) ||
+      (reinterpret_cast<uintptr_t>(scale) & 3u))
+    return FP8L_EALIGN;
+  hipError_t e = fp8l::quantize_scaled_launch(x, rows, cols, scale, q, qt,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
+int fp8_linear_bwd_w_f32(const void *dytq, const float *sdyt, const void *xtq,
+                         const float *sxt, int64_t M, int64_t N, int64_t K, int scaling,
+                         float *grad_w, void *stream) {
+  if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return FP8L_EINVAL;
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8L_ESHAPE;
+  // [N,K] fp32 = dYTq[N,M] . XTq[K,M]^T: 4-byte outputs under the same
+  // 32-bit offset limit
+  if (bad_gemm_sizes(N, K, M) || 4 * N * K > kMaxGemmBytes) return FP8L_ESHAPE;
+  int s = check_gemm_operands(dytq, sdyt, xtq, sxt, grad_w, N, K, M);
+  if (s != FP8L_OK) return s;
+  hipError_t e = fp8l::gemm_f32_launch(static_cast<const uint8_t *>(dytq), sdyt,
+                                       static_cast<const uint8_t *>(xtq), sxt,
+                                       scaling == FP8L_ROWWISE, N, K, M, grad_w,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
 int fp8_linear_encode_e4m3(const float *in, uint8_t *out, int64_t n, void *stream) {
   if (n < 0 || n > kMaxElems) return FP8L_ESHAPE;
   if (n == 0) return FP8L_OK;

@@ -50,11 +50,22 @@ hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
                            hipStream_t stream);
 hipError_t encode_launch(const float *in, uint8_t *out, int64_t n,
                          hipStream_t stream);
+// Tensorwise amax of x into amax_out[0] (workspace: the tensorwise quantize
+// workspace of the same shape).
+hipError_t amax_launch(const void *x, int64_t rows, int64_t cols, float *amax_out,
+                       void *workspace, hipStream_t stream);
+// Cast with a given tensorwise multiplier scale[0]: q and its transpose qt.
+hipError_t quantize_scaled_launch(const void *x, int64_t rows, int64_t cols,
+                                  const float *scale, void *q, void *qt, hipStream_t stream);
 
 // C[M,N] (bf16) = (A[M,K] . B[N,K]^T) * (1/sa) * (1/sb); with rowwise, sa
 // has M entries and sb N entries, else one each.
 hipError_t gemm_launch(const uint8_t *A, const float *sa, const uint8_t *B,
                        const float *sb, int rowwise, int64_t M, int64_t N,
                        int64_t K, uint16_t *C, hipStream_t stream);
+// The same GEMM with fp32 output: C32[M,N] = fl32(fl32(acc / sa) / sb).
+hipError_t gemm_f32_launch(const uint8_t *A, const float *sa, const uint8_t *B,
+                           const float *sb, int rowwise, int64_t M, int64_t N,
+                           int64_t K, float *C, hipStream_t stream);
 
 }  // namespace fp8l

@@ -145,12 +145,13 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m,
 }
 
 // KFULL: K % 128 == 0 (no K tail, no per-chunk K check).  RW: rowwise
-// scales (sa[M], sb[N]) instead of one scale per operand.
-template <bool KFULL, bool RW>
+// scales (sa[M], sb[N]) instead of one scale per operand.  F32: fp32 output
+// (the scaled value before bf16 rounding) instead of bf16.
+template <bool KFULL, bool RW, bool F32>
 __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
     const uint8_t *__restrict__ A, const float *__restrict__ sa,
     const uint8_t *__restrict__ B, const float *__restrict__ sb,
-    int M, int N, int K, uint16_t *__restrict__ C, int tiles_m, int tiles_n) {
+    int M, int N, int K, void *__restrict__ C, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[INV_OFF + (RW ? INV_BYTES : 0)];
 
   const int tid = threadIdx.x;
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
   const __amdgpu_buffer_rsrc_t rsB =
       __builtin_amdgcn_make_buffer_rsrc((void *)B, (short)0, N * K, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsC =
-      __builtin_amdgcn_make_buffer_rsrc((void *)C, (short)0, M * N * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(C, (short)0, M * N * (F32 ? 4 : 2), 0x00020000);
 
   // ---- DMA: wave w, instruction q (0..15; 0..7 A, 8..15 B) fills slab
   // rows w*64 + (q&7)*8 + lane/8.  Row r keeps logical chunk c at physical
@@ -411,6 +412,52 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
   asm volatile("" : "+v"(tid_e));
   const int lane_e = tid_e & 63;
   const int nq = (lane_e >> 4) * 4;     // first of the lane's 4 n in a block
+  if (F32) {
+    // fp32 output: two passes of 64 rows x 128 columns per wave (rows of
+    // 512 B padded to 528 B; 4 x 33 KB fits below the rowwise scale table);
+    // stores: 2 rows x 512 B per instruction, 32 lanes per row
+    constexpr int EPF_STRIDE = 528;
+    constexpr int EPF_WAVE = 64 * EPF_STRIDE;
+    static_assert(4 * EPF_WAVE <= INV_OFF, "fp32 staging overlaps the scale table");
+    uint8_t *epf = lds + wave * EPF_WAVE;
+    const int fcol = n0 + wn * WN + (lane_e & 31) * 4;
+    const bool fcol_ok = fcol < N;      // N % 16 == 0: all 4 columns or none
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int ii = 0; ii < NF / 2; ++ii) {
+        const int i = h * (NF / 2) + ii;
+        const int ml = ii * FR + (lane_e & 15);         // row within the pass
+        const float inv_a = RW ? inv[wm * WM + i * FR + (lane_e & 15)] : inv_a0;
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          const int nl = j * FR + nq;
+          v4f ib = {inv_b0, inv_b0, inv_b0, inv_b0};
+          if (RW) ib = *reinterpret_cast<const v4f *>(inv + BM + wn * WN + nl);
+          const v4f v = {(acc[j][i][0] * inv_a) * ib[0], (acc[j][i][1] * inv_a) * ib[1],
+                         (acc[j][i][2] * inv_a) * ib[2], (acc[j][i][3] * inv_a) * ib[3]};
+          *reinterpret_cast<v4f *>(epf + ml * EPF_STRIDE + nl * 4) = v;
+        }
+      }
+      const int frow0 = m0 + wm * WM + h * 64 + (lane_e >> 5);
+#pragma unroll
+      for (int it0 = 0; it0 < 32; it0 += 8) {
+        v4u v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int r = (it0 + u) * 2 + (lane_e >> 5);
+          v[u] = *reinterpret_cast<const v4u *>(epf + r * EPF_STRIDE + (lane_e & 31) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = frow0 + (it0 + u) * 2;
+          const uint32_t off = (fcol_ok && row < M) ? (uint32_t)((row * N + fcol) * 4) : OOB_C;
+          __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off, 0, 0);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
     const int ml = i * FR + (lane_e & 15);              // row within the wave tile
@@ -462,10 +509,25 @@ hipError_t gemm_launch(const uint8_t *A, const float *sa, const uint8_t *B,
   const int tiles_n = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   const bool kfull = K % BK == 0;
-  auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true> : k_gemm_fp8_tn<false, true>)
-                      : (kfull ? k_gemm_fp8_tn<true, false> : k_gemm_fp8_tn<false, false>);
+  auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true, false> : k_gemm_fp8_tn<false, true, false>)
+                      : (kfull ? k_gemm_fp8_tn<true, false, false> : k_gemm_fp8_tn<false, false, false>);
   hipLaunchKernelGGL(kern, grid, dim3(THREADS), 0, stream, A, sa, B, sb, (int)M, (int)N,
-                     (int)K, C, tiles_m, tiles_n);
+                     (int)K, (void *)C, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t gemm_f32_launch(const uint8_t *A, const float *sa, const uint8_t *B,
+                           const float *sb, int rowwise, int64_t M, int64_t N,
+                           int64_t K, float *C, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const int tiles_m = (int)((M + BM - 1) / BM);
+  const int tiles_n = (int)((N + BN - 1) / BN);
+  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  const bool kfull = K % BK == 0;
+  auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true, true> : k_gemm_fp8_tn<false, true, true>)
+                      : (kfull ? k_gemm_fp8_tn<true, false, true> : k_gemm_fp8_tn<false, false, true>);
+  hipLaunchKernelGGL(kern, grid, dim3(THREADS), 0, stream, A, sa, B, sb, (int)M, (int)N,
+                     (int)K, (void *)C, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

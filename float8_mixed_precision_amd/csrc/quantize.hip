@@ -140,6 +140,14 @@ __device__ __forceinline__ uint32_t tw_amax_bits(const uint32_t *__restrict__ pa
   return mm;
 }
 
+// Shard amax only: one block reduces the partials and stores |amax|.
+__global__ __launch_bounds__(AM_THREADS) void k_amax_finish(
+    const uint32_t *__restrict__ part, int nb, float *amax_out) {
+  __shared__ uint32_t red[AM_THREADS / 64];
+  const uint32_t am = tw_amax_bits(part, nb, red);
+  if (threadIdx.x == 0) amax_out[0] = bf16_to_f32(am);
+}
+
 // Empty tensor: the scale of amax 0.
 __global__ __launch_bounds__(64) void k_finalize_tw_empty(float *scale, float *scale_t,
                                                           float *amax_out) {
@@ -249,10 +257,12 @@ __global__ __launch_bounds__(256) void k_finalize_rowwise(
 // Phase B: each thread reads 16-byte chunks (16 rows of one column) from LDS
 // and stores them to qt: eight threads write one 128-byte qt row segment.
 //
-// Tensorwise: the block first reduces the amax pass's partial maxima to the
+// MODE_TW: the block first reduces the amax pass's partial maxima to the
 // tensor's scale; block 0 also stores it (scale, scale_t, amax_out).
-// Rowwise: scale / scale_t are inputs (from k_finalize_rowwise).
-template <bool ROWWISE>
+// MODE_RW: scale / scale_t are inputs (from k_finalize_rowwise).
+// MODE_GIVEN: scale[0] is a tensorwise multiplier given by the caller.
+constexpr int MODE_TW = 0, MODE_RW = 1, MODE_GIVEN = 2;
+template <int MODE>
 __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
     const uint16_t *__restrict__ x, int rows, int cols, int tiles_c,
     float *__restrict__ scale, float *__restrict__ scale_t,
@@ -268,12 +278,15 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
   const int rg = tid >> 4;
   const int c = c0 + c8 * 8;
   const bool col_ok = c < cols;
+  constexpr bool ROWWISE = MODE == MODE_RW;
 
   float sc[8];                    // column scales (rowwise) of the 8 columns
   float s_t = 0.f;                // tensor scale
   if (ROWWISE) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) sc[j] = col_ok ? scale_t[c + j] : 0.f;
+  } else if (MODE == MODE_GIVEN) {
+    s_t = scale[0];
   } else {
     __shared__ uint32_t red[CT_THREADS / 64];
     const uint32_t am = tw_amax_bits(part, nparts, red);
@@ -434,16 +447,39 @@ hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
   const int64_t ct_r = cdiv(rows, CT_T), ct_c = cdiv(cols, CT_T);
   if (ct_r * ct_c > 0) {
     if (scaling == FP8L_TENSORWISE)
-      hipLaunchKernelGGL(k_cast_transpose<false>, dim3((unsigned)(ct_r * ct_c)),
+      hipLaunchKernelGGL(k_cast_transpose<MODE_TW>, dim3((unsigned)(ct_r * ct_c)),
                          dim3(CT_THREADS), 0, stream, xb, R, C, (int)ct_c, scale, scale_t,
                          part, (int)nb, amax_out, static_cast<uint8_t *>(q),
                          static_cast<uint8_t *>(qt));
     else
-      hipLaunchKernelGGL(k_cast_transpose<true>, dim3((unsigned)(ct_r * ct_c)),
+      hipLaunchKernelGGL(k_cast_transpose<MODE_RW>, dim3((unsigned)(ct_r * ct_c)),
                          dim3(CT_THREADS), 0, stream, xb, R, C, (int)ct_c, scale, scale_t,
                          nullptr, 0, nullptr, static_cast<uint8_t *>(q),
                          static_cast<uint8_t *>(qt));
   }
+  return hipGetLastError();
+}
+
+hipError_t amax_launch(const void *x, int64_t rows, int64_t cols, float *amax_out,
+                       void *workspace, hipStream_t stream) {
+  const int64_t nb = tw_blocks(rows, cols);
+  uint32_t *part = static_cast<uint32_t *>(workspace);
+  if (nb > 0)
+    hipLaunchKernelGGL(k_amax_tw, dim3((unsigned)nb), dim3(AM_THREADS), 0, stream,
+                       static_cast<const uint4 *>(x), rows * cols / 8, part);
+  hipLaunchKernelGGL(k_amax_finish, dim3(1), dim3(AM_THREADS), 0, stream, part, (int)nb,
+                     amax_out);
+  return hipGetLastError();
+}
+
+hipError_t quantize_scaled_launch(const void *x, int64_t rows, int64_t cols,
+                                  const float *scale, void *q, void *qt, hipStream_t stream) {
+  const int64_t ct_r = cdiv(rows, CT_T), ct_c = cdiv(cols, CT_T);
+  if (ct_r * ct_c > 0)
+    hipLaunchKernelGGL(k_cast_transpose<MODE_GIVEN>, dim3((unsigned)(ct_r * ct_c)),
+                       dim3(CT_THREADS), 0, stream, static_cast<const uint16_t *>(x), (int)rows,
+                       (int)cols, (int)ct_c, const_cast<float *>(scale), nullptr, nullptr, 0,
+                       nullptr, static_cast<uint8_t *>(q), static_cast<uint8_t *>(qt));
   return hipGetLastError();
 }
 

@@ -22,8 +22,9 @@ LIB_PATH = os.path.join(HERE, "_lib", "libfp8linear.so")
 
 FP8L_OK, FP8L_EINVAL, FP8L_ESHAPE, FP8L_EALIGN, FP8L_EWORKSPACE, FP8L_EHIP = range(6)
 FP8L_TENSORWISE, FP8L_ROWWISE = 0, 1
-EXPORTS = ("fp8_linear_workspace_bytes", "fp8_linear_quantize", "fp8_linear_fwd",
-           "fp8_linear_bwd", "fp8_linear_encode_e4m3", "fp8_linear_status_string",
+EXPORTS = ("fp8_linear_workspace_bytes", "fp8_linear_quantize", "fp8_linear_amax",
+           "fp8_linear_quantize_scaled", "fp8_linear_fwd", "fp8_linear_bwd",
+           "fp8_linear_bwd_w_f32", "fp8_linear_encode_e4m3", "fp8_linear_status_string",
            "fp8_linear_version")
 
 
@@ -54,6 +55,12 @@ def lib() -> ctypes.CDLL:
     L.fp8_linear_fwd.argtypes = [P, P, P, P, i64, i64, i64, I, P, P]
     L.fp8_linear_bwd.restype = I
     L.fp8_linear_bwd.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, I, P, P, P]
+    L.fp8_linear_amax.restype = I
+    L.fp8_linear_amax.argtypes = [P, i64, i64, P, P, ctypes.c_size_t, P]
+    L.fp8_linear_quantize_scaled.restype = I
+    L.fp8_linear_quantize_scaled.argtypes = [P, i64, i64, P, P, P, P]
+    L.fp8_linear_bwd_w_f32.restype = I
+    L.fp8_linear_bwd_w_f32.argtypes = [P, P, P, P, i64, i64, i64, I, P, P]
     L.fp8_linear_encode_e4m3.restype = I
     L.fp8_linear_encode_e4m3.argtypes = [P, P, i64, P]
     L.fp8_linear_status_string.restype = ctypes.c_char_p
@@ -164,6 +171,49 @@ def fp8_linear_bwd(dyq, sdy, dytq, sdyt, wtq, swt, xtq, sxt, M: int, N: int, K: 
                                 _p(grad_w if want_w else None), _stream(stream)),
            "fp8_linear_bwd")
     return grad_x, grad_w
+
+
+def fp8_linear_amax(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """[1] fp32 max |x| of a bf16 matrix (one shard's share of a global amax)."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(rows, cols, False, x.device)
+    _check(lib().fp8_linear_amax(_p(x), rows, cols, _p(out), _p(workspace), workspace.numel(),
+                                 _stream(stream)), "fp8_linear_amax")
+    return out
+
+
+def fp8_linear_quantize_scaled(x: torch.Tensor, scale: torch.Tensor,
+                               q: Optional[torch.Tensor] = None,
+                               qt: Optional[torch.Tensor] = None,
+                               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(q [rows, cols], qt [cols, rows]) E4M3 codes of x * scale[0]."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
+    assert scale.dtype == torch.float32 and scale.numel() >= 1
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    _check(lib().fp8_linear_quantize_scaled(_p(x), rows, cols, _p(scale), _p(q), _p(qt),
+                                            _stream(stream)), "fp8_linear_quantize_scaled")
+    return q, qt
+
+
+def fp8_linear_bwd_w_f32(dytq, sdyt, xtq, sxt, M: int, N: int, K: int,
+                         rowwise: bool = False, grad_w: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """grad_w [N, K] fp32 = dY^T . X from the fp8 copies (no bf16 rounding)."""
+    if grad_w is None:
+        grad_w = torch.empty((N, K), dtype=torch.float32, device=dytq.device)
+    _check(lib().fp8_linear_bwd_w_f32(_p(dytq), _p(sdyt), _p(xtq), _p(sxt), M, N, K,
+                                      _scaling(rowwise), _p(grad_w), _stream(stream)),
+           "fp8_linear_bwd_w_f32")
+    return grad_w
 
 
 def fp8_linear_encode_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -111,6 +111,40 @@ FP8L_API int fp8_linear_quantize(const void *x, int64_t rows, int64_t cols, int 
                         void *stream);
 
 /*
+ * Tensorwise amax of one bf16 matrix alone: one GPU's share of the global
+ * amax that Float8 all-gather of FSDP2 weights needs ("Enabling Float8
+ * All-Gather in FSDP2" on the torchtitan forum index: each rank reduces its
+ * shard, an all-reduce(max) of the 4-byte amax makes the tensorwise scale
+ * global, then every rank casts its shard with that scale).
+ *
+ *   x         [rows, cols] bf16 (device, read only)
+ *   amax_out  [1] fp32 (device, written): max |x|, NaN if x holds a NaN,
+ *             0 for an empty x
+ *   workspace / workspace_bytes: as for fp8_linear_quantize with
+ *             FP8L_TENSORWISE and the same shape.
+ */
+FP8L_API int fp8_linear_amax(const void *x, int64_t rows, int64_t cols, float *amax_out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Cast with a scale given by the caller (single read pass, 4 bytes of HBM
+ * traffic per element): the second half of the Float8 all-gather flow above,
+ * or any recipe whose scale is known before the cast.
+ *
+ *   q[r][c]  = e4m3_sat_rne( fp32(x[r][c] * scale[0]) ),  qt[c][r] = q[r][c]
+ *
+ *   x      [rows, cols] bf16 (device, read only)
+ *   scale  [1] fp32 multiplier (device, read only), e.g.
+ *          448 / max(global_amax, 1e-12) computed as one fp32 division
+ *   q      [rows, cols] e4m3 bytes (device, written)
+ *   qt     [cols, rows] e4m3 bytes (device, written)
+ * An empty x writes nothing.  Same shape and alignment rules as
+ * fp8_linear_quantize.
+ */
+FP8L_API int fp8_linear_quantize_scaled(const void *x, int64_t rows, int64_t cols,
+                                        const float *scale, void *q, void *qt, void *stream);
+
+/*
  * Forward GEMM of the linear (out = X . W^T) on the quantized operands:
  *
  *   out[m][n] = bf16( fp32( fp32(acc * (1/sx)) * (1/sw) ) ),
@@ -145,6 +179,24 @@ FP8L_API int fp8_linear_bwd(const void *dyq, const float *sdy, const void *dytq,
                    const void *xtq, const float *sxt, int64_t M, int64_t N,
                    int64_t K, int scaling, void *grad_x, void *grad_w,
                    void *stream);
+
+/*
+ * grad_W of the linear with an fp32 output: the value before bf16 rounding,
+ * for a grad_W that is reduce-scattered in fp32 (the torchtitan tutorial,
+ * Part IV, Stage 5: gradients are reduced in float32 under the default
+ * mixed-precision policy).
+ *
+ *   grad_w[n][k] = fp32( fp32(acc / sdyt) / sxt ),
+ *   acc = sum_m value(dytq[n][m]) * value(xtq[k][m])     (fp32 accumulate)
+ *
+ * with the reciprocals 1/sdyt, 1/sxt taken in fp32 and multiplied as in
+ * fp8_linear_bwd (so bf16(grad_w) is fp8_linear_bwd's grad_w).  Operands,
+ * scales and scaling as for fp8_linear_bwd's grad_w; grad_w [N, K] fp32
+ * (device, written), 16-byte aligned, N * K * 4 < 2^31 bytes.
+ */
+FP8L_API int fp8_linear_bwd_w_f32(const void *dytq, const float *sdyt, const void *xtq,
+                                  const float *sxt, int64_t M, int64_t N, int64_t K,
+                                  int scaling, float *grad_w, void *stream);
 
 /*
  * The element conversion the quantize kernels use, exposed for testing it on

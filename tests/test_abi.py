@@ -142,3 +142,46 @@ def test_encode_rejects_bad_arguments():
     assert L.fp8_linear_encode_e4m3(None, P(A16), 4, None) == ops.FP8L_EINVAL
     assert L.fp8_linear_encode_e4m3(P(A_BAD), P(A16), 4, None) == ops.FP8L_EALIGN
     assert L.fp8_linear_encode_e4m3(None, None, 0, None) == ops.FP8L_OK   # empty
+
+
+@pytestmark_cpu
+def test_amax_scaled_and_f32_entry_points_reject_bad_arguments():
+    E = ops
+    L = ops.lib()
+    P = ctypes.c_void_p
+
+    def amax(x=A16, rows=16, cols=16, out=A16, ws=A16, wsb=1 << 20):
+        return L.fp8_linear_amax(P(x) if x else None, rows, cols, P(out) if out else None,
+                                 P(ws) if ws else None, wsb, None)
+
+    assert amax(rows=24) == E.FP8L_ESHAPE
+    assert amax(out=None) == E.FP8L_EINVAL
+    assert amax(x=None) == E.FP8L_EINVAL
+    assert amax(ws=None) == E.FP8L_EINVAL
+    assert amax(wsb=0) == E.FP8L_EWORKSPACE
+    assert amax(x=A_BAD) == E.FP8L_EALIGN
+    assert amax(out=A16 + 2) == E.FP8L_EALIGN
+
+    def qs(x=A16, rows=16, cols=16, s=A16, q=A16, qt=A16):
+        return L.fp8_linear_quantize_scaled(P(x) if x else None, rows, cols,
+                                            P(s) if s else None, P(q) if q else None,
+                                            P(qt) if qt else None, None)
+
+    assert qs(cols=8) == E.FP8L_ESHAPE
+    assert qs(rows=0, x=None, s=None, q=None, qt=None) == E.FP8L_OK   # empty: nothing to do
+    assert qs(s=None) == E.FP8L_EINVAL
+    assert qs(q=None) == E.FP8L_EINVAL
+    assert qs(qt=A_BAD) == E.FP8L_EALIGN
+    assert qs(s=A16 + 1) == E.FP8L_EALIGN
+
+    def bw(dyt=A16, sdyt=A16, xt=A16, sxt=A16, M=16, N=16, K=16, scaling=0, gw=A16):
+        return L.fp8_linear_bwd_w_f32(P(dyt) if dyt else None, P(sdyt) if sdyt else None,
+                                      P(xt) if xt else None, P(sxt) if sxt else None,
+                                      M, N, K, scaling, P(gw) if gw else None, None)
+
+    assert bw(scaling=3) == E.FP8L_EINVAL
+    assert bw(N=40) == E.FP8L_ESHAPE
+    assert bw(N=32768, K=32768) == E.FP8L_ESHAPE        # 4 GiB of fp32 output
+    assert bw(gw=None) == E.FP8L_EINVAL
+    assert bw(sxt=None) == E.FP8L_EINVAL
+    assert bw(gw=A_BAD) == E.FP8L_EALIGN
