@@ -70,6 +70,17 @@ class Oracle:
                                     i64, i64, i64, P, P]
         lib.orc_gemm_tn_sampled.argtypes = [P, P, ctypes.c_int, P, P,
                                             ctypes.c_int, i64, P, P, i64, P, P]
+        lib.orc_e5m2_value.restype = ctypes.c_double
+        lib.orc_e5m2_value.argtypes = [ctypes.c_uint8]
+        lib.orc_e5m2_encode_array.argtypes = [P, P, i64]
+        lib.orc_scale_from_amax_e5m2.restype = ctypes.c_float
+        lib.orc_scale_from_amax_e5m2.argtypes = [ctypes.c_float]
+        lib.orc_quantize_e5m2.argtypes = [P, i64, i64, ctypes.c_int, P, P, P, P, P]
+        lib.orc_gemm_tn_mixed.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int,
+                                          P, ctypes.c_int, i64, i64, i64, P]
+        lib.orc_gemm_tn_mixed_sampled.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P,
+                                                  ctypes.c_int, P, ctypes.c_int, i64, P, P,
+                                                  i64, P]
         lib.orc_amax.restype = ctypes.c_float
         lib.orc_amax.argtypes = [P, i64]
         lib.orc_quantize_scaled.argtypes = [P, i64, i64, ctypes.c_float, P, P]
@@ -143,6 +154,36 @@ class Oracle:
                               _ptr(qt), _ptr(s), _ptr(st), _ptr(am))
         return q, qt, s, st, am
 
+    # -------------------------------------------------------------- e5m2 --
+    def e5m2_values(self) -> np.ndarray:
+        """float64 value of each of the 256 E5M2 codes (closed form)."""
+        return np.array([self.lib.orc_e5m2_value(c) for c in range(256)], np.float64)
+
+    def e5m2_encode(self, y) -> np.ndarray:
+        """Saturating RNE E5M2 codes of fp32 values (any shape)."""
+        y = _c(y, np.float32)
+        out = np.empty(y.shape, dtype=np.uint8)
+        self.lib.orc_e5m2_encode_array(_ptr(y), _ptr(out), y.size)
+        return out
+
+    def scale_from_amax_e5m2(self, a: float) -> np.float32:
+        """fp32 scale 57344 / max(a, 1e-12), one IEEE division."""
+        return np.float32(self.lib.orc_scale_from_amax_e5m2(float(np.float32(a))))
+
+    def quantize_e5m2(self, x_bits, rowwise: bool = False):
+        """quantize() with E5M2 codes and scales mapping amax onto 57344."""
+        x = _c(x_bits, np.uint16)
+        rows, cols = x.shape
+        q = np.empty((rows, cols), dtype=np.uint8)
+        qt = np.empty((cols, rows), dtype=np.uint8)
+        n_s, n_st, n_a = (rows, cols, rows + cols) if rowwise else (1, 1, 1)
+        s = np.empty(n_s, np.float32)
+        st = np.empty(n_st, np.float32)
+        am = np.empty(n_a, np.float32)
+        self.lib.orc_quantize_e5m2(_ptr(x), rows, cols, int(bool(rowwise)), _ptr(q),
+                                   _ptr(qt), _ptr(s), _ptr(st), _ptr(am))
+        return q, qt, s, st, am
+
     def amax(self, x_bits) -> np.float32:
         """max |x| over a bf16 tensor (NaN-propagating; 0 for an empty one)."""
         x = _c(x_bits, np.uint16)
@@ -204,6 +245,38 @@ class Oracle:
                                      _ptr(ii), _ptr(jj), ii.size, _ptr(out),
                                      _ptr(acc))
         return (out, acc) if return_acc else out
+
+    def gemm_tn_mixed(self, a, fmt_a, sa, b, fmt_b, sb):
+        """gemm_tn with a code format per operand (0 = E4M3, 1 = E5M2)."""
+        a = _c(a, np.uint8)
+        b = _c(b, np.uint8)
+        sa = _c(np.atleast_1d(sa), np.float32)
+        sb = _c(np.atleast_1d(sb), np.float32)
+        m, k = a.shape
+        n, k2 = b.shape
+        assert k == k2 and sa.size in (1, m) and sb.size in (1, n)
+        out = np.empty((m, n), dtype=np.uint16)
+        self.lib.orc_gemm_tn_mixed(_ptr(a), int(fmt_a), _ptr(sa), int(sa.size != 1), _ptr(b),
+                                   int(fmt_b), _ptr(sb), int(sb.size != 1), m, n, k, _ptr(out))
+        return out
+
+    def gemm_tn_mixed_sampled(self, a, fmt_a, sa, b, fmt_b, sb, ii, jj):
+        a = _c(a, np.uint8)
+        b = _c(b, np.uint8)
+        sa = _c(np.atleast_1d(sa), np.float32)
+        sb = _c(np.atleast_1d(sb), np.float32)
+        ii = _c(ii, np.int64)
+        jj = _c(jj, np.int64)
+        m, k = a.shape
+        n, k2 = b.shape
+        assert k == k2 and ii.shape == jj.shape and sa.size in (1, m) and sb.size in (1, n)
+        if ii.size:
+            assert ii.min() >= 0 and ii.max() < m and jj.min() >= 0 and jj.max() < n
+        out = np.empty(ii.shape, dtype=np.uint16)
+        self.lib.orc_gemm_tn_mixed_sampled(_ptr(a), int(fmt_a), _ptr(sa), int(sa.size != 1),
+                                           _ptr(b), int(fmt_b), _ptr(sb), int(sb.size != 1),
+                                           k, _ptr(ii), _ptr(jj), ii.size, _ptr(out))
+        return out
 
     def gemm_tn_f32(self, a, sa, b, sb):
         """fp32 form of gemm_tn: fl32(fl32(acc * (1/sa_i)) * (1/sb_j)), no
@@ -292,6 +365,30 @@ def gemm_tn_sampled(a, sa, b, sb, ii, jj, return_acc=False):
 
 def amax(x_bits):
     return default().amax(x_bits)
+
+
+def e5m2_values():
+    return default().e5m2_values()
+
+
+def e5m2_encode(y):
+    return default().e5m2_encode(y)
+
+
+def scale_from_amax_e5m2(a):
+    return default().scale_from_amax_e5m2(a)
+
+
+def quantize_e5m2(x_bits, rowwise=False):
+    return default().quantize_e5m2(x_bits, rowwise)
+
+
+def gemm_tn_mixed(a, fmt_a, sa, b, fmt_b, sb):
+    return default().gemm_tn_mixed(a, fmt_a, sa, b, fmt_b, sb)
+
+
+def gemm_tn_mixed_sampled(a, fmt_a, sa, b, fmt_b, sb, ii, jj):
+    return default().gemm_tn_mixed_sampled(a, fmt_a, sa, b, fmt_b, sb, ii, jj)
 
 
 def quantize_scaled(x_bits, scale):

@@ -38,6 +38,7 @@
 #include <string.h>
 
 #define ORC_E4M3_MAX 448.0
+#define ORC_E5M2_MAX 57344.0
 #define ORC_EPS 1e-12f
 
 /* ---------------------------------------------------------------- e4m3 -- */
@@ -57,10 +58,28 @@ double orc_e4m3_value(uint8_t code)
     return s ? -mag : mag;
 }
 
-/* The closed form evaluated once per code, so the hot loops below read a
+/* Value of an E5M2 code from its closed form (OCP E5M2, the second
+ * encoding of the same FP8 formats paper, IEEE-like):
+ *   S = bit 7, E = bits 6..2, F = bits 1..0
+ *   E == 31: F == 0 -> (-1)^S * inf, otherwise NaN
+ *   E == 0          -> (-1)^S * F * 2^-16          (subnormals, +-0)
+ *   otherwise       -> (-1)^S * (4 + F) * 2^(E-17)                         */
+double orc_e5m2_value(uint8_t code)
+{
+    int s = code >> 7, e = (code >> 2) & 31, f = code & 3;
+    double mag;
+    if (e == 31) mag = f == 0 ? INFINITY : NAN;
+    else if (e == 0) mag = ldexp((double)f, -16);
+    else mag = ldexp((double)(4 + f), e - 17);
+    return s ? -mag : mag;
+}
+
+/* The closed forms evaluated once per code, so the hot loops below read a
  * table instead of calling ldexp. */
 static double val64[256];
 static float val32[256];
+static double e5_val64[256];
+static float e5_val32[256];
 static int tables_ready;
 
 static void tables_init(void)
@@ -69,6 +88,8 @@ static void tables_init(void)
     for (int c = 0; c < 256; c++) {
         val64[c] = orc_e4m3_value((uint8_t)c);
         val32[c] = (float)val64[c];
+        e5_val64[c] = orc_e5m2_value((uint8_t)c);
+        e5_val32[c] = (float)e5_val64[c];
     }
     tables_ready = 1;
 }
@@ -107,6 +128,38 @@ void orc_e4m3_encode_array(const float *y, uint8_t *out, int64_t n)
     tables_init();
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; i++) out[i] = orc_e4m3_encode(y[i]);
+}
+
+/* Saturating round-to-nearest-even E5M2 encode, the same definition as for
+ * E4M3 with this format's finite values: nearest finite value, ties to the
+ * code whose last bit is 0, magnitudes at or above 57344 (and +-inf) clamp
+ * to the largest finite code 0x7B, the sign bit from y, NaN -> 0x7F. */
+uint8_t orc_e5m2_encode(float y)
+{
+    tables_init();
+    uint8_t sgn = signbit(y) ? (uint8_t)0x80 : (uint8_t)0x00;
+    if (isnan(y)) return (uint8_t)(sgn | 0x7F);
+    double m = fabs((double)y);
+    if (m >= ORC_E5M2_MAX) return (uint8_t)(sgn | 0x7B);
+    int lo = 0, hi = 0x7B;            /* e5 value(lo) <= m < e5 value(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (e5_val64[mid] <= m) lo = mid; else hi = mid;
+    }
+    double dlo = m - e5_val64[lo];
+    double dhi = e5_val64[hi] - m;
+    int code;
+    if (dlo < dhi)      code = lo;
+    else if (dhi < dlo) code = hi;
+    else                code = (lo & 1) ? hi : lo;
+    return (uint8_t)(sgn | code);
+}
+
+void orc_e5m2_encode_array(const float *y, uint8_t *out, int64_t n)
+{
+    tables_init();
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) out[i] = orc_e5m2_encode(y[i]);
 }
 
 /* ---------------------------------------------------------------- bf16 -- */
@@ -252,6 +305,62 @@ void orc_quantize_scaled(const uint16_t *x, int64_t rows, int64_t cols, float s,
         }
 }
 
+/* s = 57344 / max(a, eps) as one IEEE fp32 division (E5M2's largest finite
+ * value in place of E4M3's 448). */
+float orc_scale_from_amax_e5m2(float a)
+{
+    float d = (a < ORC_EPS) ? ORC_EPS : a;
+    return (float)ORC_E5M2_MAX / d;
+}
+
+/* The quantize of orc_quantize with E5M2 codes (gradients): the same
+ * amax / scale / cast steps, the scale mapping amax onto 57344. */
+void orc_quantize_e5m2(const uint16_t *x, int64_t rows, int64_t cols, int rowwise,
+                       uint8_t *q, uint8_t *qt, float *scale, float *scale_t,
+                       float *amax)
+{
+    tables_init();
+    if (!rowwise) {
+        float a = 0.0f;
+        for (int64_t i = 0; i < rows * cols; i++)
+            a = amax_update(a, orc_bf16_to_f32(x[i]));
+        float s = orc_scale_from_amax_e5m2(a);
+        #pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < rows; r++)
+            for (int64_t c = 0; c < cols; c++) {
+                uint8_t code = orc_e5m2_encode(orc_bf16_to_f32(x[r * cols + c]) * s);
+                q[r * cols + c] = code;
+                qt[c * rows + r] = code;
+            }
+        scale[0] = s;
+        scale_t[0] = s;
+        if (amax) amax[0] = a;
+        return;
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        float a = 0.0f;
+        for (int64_t c = 0; c < cols; c++)
+            a = amax_update(a, orc_bf16_to_f32(x[r * cols + c]));
+        float s = orc_scale_from_amax_e5m2(a);
+        for (int64_t c = 0; c < cols; c++)
+            q[r * cols + c] = orc_e5m2_encode(orc_bf16_to_f32(x[r * cols + c]) * s);
+        scale[r] = s;
+        if (amax) amax[r] = a;
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; c++) {
+        float a = 0.0f;
+        for (int64_t r = 0; r < rows; r++)
+            a = amax_update(a, orc_bf16_to_f32(x[r * cols + c]));
+        float s = orc_scale_from_amax_e5m2(a);
+        for (int64_t r = 0; r < rows; r++)
+            qt[c * rows + r] = orc_e5m2_encode(orc_bf16_to_f32(x[r * cols + c]) * s);
+        scale_t[c] = s;
+        if (amax) amax[rows + c] = a;
+    }
+}
+
 /* ---------------------------------------------------------------- GEMM -- */
 
 /* One output element of a scaled fp8 GEMM with both operands contiguous
@@ -339,5 +448,53 @@ void orc_gemm_tn_f32_sampled(const uint8_t *a, const float *sa, int a_vec,
         int64_t i = ii[s], j = jj[s];
         out[s] = gemm_element_f32(a + i * k, b + j * k, k,
                                   a_vec ? sa[i] : sa[0], b_vec ? sb[j] : sb[0], 0);
+    }
+}
+
+/* The GEMM with a format per operand (0 = E4M3, 1 = E5M2), e.g. an E5M2
+ * gradient times an E4M3 weight or activation; every E4M3 x E5M2 product
+ * has at most 7 significant bits and is exact in fp32, so the definition is
+ * otherwise the same: fp32 sum in ascending t, fp32 reciprocals, bf16. */
+static uint16_t gemm_element_mixed(const uint8_t *arow, const float *ta,
+                                   const uint8_t *brow, const float *tb,
+                                   int64_t k, float sa, float sb)
+{
+    float sum = 0.0f;
+    for (int64_t t = 0; t < k; ++t)
+        sum += ta[arow[t]] * tb[brow[t]];
+    float ra = 1.0f / sa;
+    float rb = 1.0f / sb;
+    float v = sum * ra;
+    v = v * rb;
+    return orc_f32_to_bf16(v);
+}
+
+void orc_gemm_tn_mixed(const uint8_t *a, int fmt_a, const float *sa, int a_vec,
+                       const uint8_t *b, int fmt_b, const float *sb, int b_vec,
+                       int64_t m, int64_t n, int64_t k, uint16_t *out)
+{
+    tables_init();
+    const float *ta = fmt_a ? e5_val32 : val32;
+    const float *tb = fmt_b ? e5_val32 : val32;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; i++)
+        for (int64_t j = 0; j < n; j++)
+            out[i * n + j] = gemm_element_mixed(a + i * k, ta, b + j * k, tb, k,
+                                                a_vec ? sa[i] : sa[0], b_vec ? sb[j] : sb[0]);
+}
+
+void orc_gemm_tn_mixed_sampled(const uint8_t *a, int fmt_a, const float *sa, int a_vec,
+                               const uint8_t *b, int fmt_b, const float *sb, int b_vec,
+                               int64_t k, const int64_t *ii, const int64_t *jj,
+                               int64_t ns, uint16_t *out)
+{
+    tables_init();
+    const float *ta = fmt_a ? e5_val32 : val32;
+    const float *tb = fmt_b ? e5_val32 : val32;
+    #pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t s = 0; s < ns; s++) {
+        int64_t i = ii[s], j = jj[s];
+        out[s] = gemm_element_mixed(a + i * k, ta, b + j * k, tb, k,
+                                    a_vec ? sa[i] : sa[0], b_vec ? sb[j] : sb[0]);
     }
 }

@@ -466,9 +466,142 @@ def check_gemm_f32(o, seed: int = 15) -> None:
     assert np.array_equal(o.gemm_tn_f32(a, sa, b, sb).astype(np.float64), ex)
 
 
+# ---------------------------------------------------------------- e5m2 --
+
+def torch_e5m2_values() -> np.ndarray:
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e5m2).to(torch.float32).double().numpy()
+
+
+def torch_encode_sat_e5m2(y: np.ndarray) -> np.ndarray:
+    """Saturating E5M2 encode via torch: clamp to +-57344, then torch's RNE
+    cast (which on its own overflows to inf)."""
+    t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32))
+    return t.clamp(-57344.0, 57344.0).to(torch.float8_e5m2).view(torch.uint8).numpy()
+
+
+def check_e5m2_decode(o) -> None:
+    """All 256 codes against torch's float8_e5m2, plus the format's facts:
+    largest finite 57344, smallest normal 2^-14, smallest subnormal 2^-16,
+    +-inf at S.11111.00, NaN at S.11111.{01,10,11}."""
+    got = o.e5m2_values()
+    ref = torch_e5m2_values()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x7B] == 57344.0 and got[0x04] == 2.0 ** -14 and got[0x01] == 2.0 ** -16
+    assert np.isposinf(got[0x7C]) and np.isneginf(got[0xFC])
+    assert np.flatnonzero(nan).tolist() == [0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF]
+
+
+def check_e5m2_encode(o, n: int = 1 << 21, seed: int = 16) -> None:
+    """Random fp32 patterns, values around every code and the rounding
+    midpoints against torch's saturating cast; nearest-value brute force
+    (ties to the even code) on a sample; sign symmetry."""
+    rng = np.random.default_rng(seed)
+    ev = torch_e5m2_values()
+    fin = ev[:0x7C]
+    mids = (fin[:-1] + fin[1:]) / 2
+    y = np.concatenate([
+        f32_from_bits(rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)),
+        fin.astype(np.float32), mids.astype(np.float32),
+        (mids * (1 + 2.0 ** -20)).astype(np.float32), (mids * (1 - 2.0 ** -20)).astype(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 57344.0, 61440.0, 1e30, 2.0 ** -17, 2.0 ** -18,
+                  3 * 2.0 ** -18], np.float32)])
+    y = np.concatenate([y, -y])
+    got = o.e5m2_encode(y)
+    nan = np.isnan(y)
+    assert np.all((got[nan] & 0x7F) > 0x7C), "NaN must give a NaN code"
+    assert np.array_equal(got[~nan], torch_encode_sat_e5m2(y[~nan]))
+    # brute force on a sample of finite values
+    ys = y[~nan][rng.integers(0, int((~nan).sum()), 4000)]
+    m = np.abs(ys.astype(np.float64))
+    d = np.abs(m[:, None] - fin[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    codes = np.arange(fin.size)
+    even = cand & (codes[None, :] % 2 == 0)
+    pick = np.where(even.any(axis=1), np.argmax(even, axis=1), np.argmax(cand, axis=1))
+    pick = np.where(m >= 57344.0, 0x7B, pick)
+    want = (pick | (np.signbit(ys).astype(np.int64) << 7)).astype(np.uint8)
+    assert np.array_equal(o.e5m2_encode(ys), want)
+
+
+def _independent_quantize_fmt(xb, rowwise, fmax, enc):
+    """_independent_quantize for another format (largest finite fmax)."""
+    x = torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16).float()
+    ax = x.abs().numpy()
+    eps = np.float64(np.float32(1e-12))
+
+    def sc(a):
+        return (fmax / np.maximum(np.asarray(a, np.float64), eps)).astype(np.float32)
+
+    if not rowwise:
+        a = np.float32(ax.max()) if ax.size else np.float32(0)
+        s = sc(a)
+        q = enc((x * torch.tensor(s)).numpy())
+        return q, q.T.copy(), np.array([s]), np.array([s]), np.array([a])
+    ar, ac = ax.max(axis=1), ax.max(axis=0)
+    sr, scol = sc(ar), sc(ac)
+    q = enc((x * torch.from_numpy(sr)[:, None]).numpy())
+    qt = enc((x * torch.from_numpy(scol)[None, :]).numpy()).T.copy()
+    return q, qt, sr, scol, np.concatenate([ar, ac]).astype(np.float32)
+
+
+def check_quantize_e5m2(o, seed: int = 17) -> None:
+    from float8_mixed_precision_amd.workloads import random_bf16
+    for si, shp in enumerate(((64, 48), (37, 16), (128, 80))):
+        for xb in (random_bf16(seed, shp, 1e-2, si), random_bf16(seed, shp, 3.0, si + 10)):
+            for rowwise in (False, True):
+                got = o.quantize_e5m2(xb, rowwise)
+                ref = _independent_quantize_fmt(xb, rowwise, 57344.0, torch_encode_sat_e5m2)
+                for name, g, r in zip(("q", "qt", "scale", "scale_t", "amax"), got, ref):
+                    g, r = np.asarray(g), np.asarray(r)
+                    if g.dtype == np.float32:
+                        g, r = _bits(g), _bits(r)
+                    assert g.shape == r.shape and np.array_equal(g, r), \
+                        "e5m2 %s differs (shape %s rowwise %s)" % (name, shp, rowwise)
+
+
+def check_gemm_mixed(o, seed: int = 18) -> None:
+    """E5M2 x E4M3: (0, 0) is the pinned E4M3 GEMM; exact sums with
+    power-of-two scales give bf16(exact / (sa sb)) exactly; general values
+    stay within one bf16 ulp of the float64 value outside cancellations;
+    sampled equals full."""
+    from oracle import bf16_ulp_distance
+    t4 = torch_e4m3_values()
+    t5 = torch_e5m2_values()
+    rng = np.random.default_rng(seed)
+    m, n, k = 24, 40, 96
+    a = random_codes(rng, (m, k))
+    b = random_codes(rng, (n, k))
+    sa = (rng.random(m) + 0.5).astype(np.float32)
+    sb = (rng.random(n) + 0.5).astype(np.float32)
+    assert np.array_equal(o.gemm_tn_mixed(a, 0, sa, b, 0, sb), o.gemm_tn(a, sa, b, sb))
+    # exact: E5M2 values in [1, 8), E4M3 in [1, 16), k = 64
+    a5 = random_codes(rng, (12, 64), 0x3C, 0x47)
+    b4 = random_codes(rng, (20, 64), 0x38, 0x57)
+    sa2 = (2.0 ** rng.integers(-4, 5, 12)).astype(np.float32)
+    sb2 = (2.0 ** rng.integers(-4, 5, 20)).astype(np.float32)
+    ex = (t5[a5] @ t4[b4].T) / (sa2[:, None].astype(np.float64) * sb2[None, :])
+    assert np.array_equal(o.gemm_tn_mixed(a5, 1, sa2, b4, 0, sb2),
+                          torch_bf16_bits(ex.astype(np.float32)))
+    # general E5M2 codes (finite: magnitudes 0x00..0x7B)
+    a5 = random_codes(rng, (m, k), 0x00, 0x7B)
+    out = o.gemm_tn_mixed(a5, 1, sa, b, 0, sb)
+    exact = t5[a5] @ t4[b].T
+    want = torch_bf16_bits((exact / (sa[:, None].astype(np.float64) * sb[None, :])).astype(np.float32))
+    cancel = np.abs(exact) < 1e-3 * (np.abs(t5[a5]) @ np.abs(t4[b]).T)
+    assert np.all(bf16_ulp_distance(out, want)[~cancel] <= 1)
+    ii = rng.integers(0, m, 300)
+    jj = rng.integers(0, n, 300)
+    assert np.array_equal(o.gemm_tn_mixed_sampled(a5, 1, sa, b, 0, sb, ii, jj), out[ii, jj])
+
+
 ALL_CHECKS = [check_decode, check_encode_random, check_encode_brute_force,
               check_encode_invariants, check_bf16, check_scale,
               check_quantize_vs_library, check_quantize_invariants,
               check_gemm_vs_exact, check_gemm_exact_cases, check_gemm_scales,
               check_gemm_tiny_brute_force, check_gemm_sampled, check_amax,
-              check_quantize_scaled, check_gemm_f32]
+              check_quantize_scaled, check_gemm_f32, check_e5m2_decode,
+              check_e5m2_encode, check_quantize_e5m2, check_gemm_mixed]

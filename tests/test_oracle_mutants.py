@@ -47,8 +47,17 @@ MUTANTS = {
     "scaled_no_scale": ("float y = orc_bf16_to_f32(x[r * cols + c]) * s;",
                         "float y = orc_bf16_to_f32(x[r * cols + c]);"),
     # cast with a given scale: qt rows reversed
-    "scaled_qt_index": ("            qt[c * rows + r] = code;\n        }\n}\n\n/* ----",
-                        "            qt[c * rows + (rows - 1 - r)] = code;\n        }\n}\n\n/* ----"),
+    "scaled_qt_index": ("uint8_t code = orc_e4m3_encode(y);\n            q[r * cols + c] = code;\n            qt[c * rows + r] = code;",
+                        "uint8_t code = orc_e4m3_encode(y);\n            q[r * cols + c] = code;\n            qt[c * rows + (rows - 1 - r)] = code;"),
+    # E5M2 decode: subnormal exponent off by one
+    "e5m2_subnormal": ("else if (e == 0) mag = ldexp((double)f, -16);",
+                       "else if (e == 0) mag = ldexp((double)f, -17);"),
+    # E5M2 encode: overflow to infinity instead of saturation
+    "e5m2_no_saturation": ("return (uint8_t)(sgn | 0x7B);", "return (uint8_t)(sgn | 0x7C);"),
+    # E5M2 quantize: the E4M3 maximum in the scale
+    "e5m2_scale_max": ("return (float)ORC_E5M2_MAX / d;", "return (float)ORC_E4M3_MAX / d;"),
+    # mixed GEMM: B decoded with A's format
+    "gemm_mixed_table": ("sum += ta[arow[t]] * tb[brow[t]];", "sum += ta[arow[t]] * ta[brow[t]];"),
     # fp32 GEMM: output stored transposed
     "gemm_f32_store": ("out[i * n + j] = gemm_element_f32(", "out[j * m + i] = gemm_element_f32("),
 }
