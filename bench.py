@@ -123,6 +123,33 @@ def cpu_baseline(wl, rows_g: int, rows_q: int = 512):
                       "%.1f s per step" % (rows_q, rows_g, flops_sampled / 1e9, wall, est)}
 
 
+def measure_e5m2_step(steps, flops_per_step: int, reps: int = 10):
+    """The whole step again with the gradient dY quantized to E5M2 and the
+    backward GEMMs reading it so (same buffers, warmed first); wall time
+    bracketed by device synchronisation, like `value`."""
+    import torch
+    for ls in steps:
+        ls.e5m2_grad = True
+    try:
+        for _ in range(2):
+            for ls in steps:
+                ls.run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for ls in steps:
+                ls.run()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+    finally:
+        for ls in steps:
+            ls.e5m2_grad = False
+    v = flops_per_step * reps / el / 1e12
+    return {"metric": "whole step, dY in E5M2 (backward GEMMs E5M2 x E4M3)",
+            "value": round(v, 2), "unit": "TFLOP/s", "steps": reps,
+            "ms_per_step": round(el * 1e3 / reps, 4)}
+
+
 def measure_next_rows(steps, stream, reps: int = 5):
     """The entry points beyond the linear's own step, timed on the same FFN
     tensors after the main measurement (outside `value`): the shard amax and
@@ -307,6 +334,7 @@ def main():
     }
     print("[bench] next rows", file=sys.stderr, flush=True)
     result["next_rows"] = measure_next_rows(steps, stream)
+    result["next_rows"]["e5m2_grad_step"] = measure_e5m2_step(steps, wl.flops)
     del steps, shared
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

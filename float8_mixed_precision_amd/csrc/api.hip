@@ -9,6 +9,9 @@ bool bad_dim(int64_t d) { return d < 0 || (d % 16) != 0 || d > (int64_t)1 << 30;
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// FP8L_TENSORWISE or FP8L_ROWWISE, optionally with the FP8L_E5M2 flag
+bool bad_scaling(int scaling) { return (scaling & ~(FP8L_ROWWISE | FP8L_E5M2)) != 0; }
+
 // Dimensions are capped at 2^30 so that every 32-bit index in the kernels
 // stays in range (addresses are formed in 64 bits), and a matrix at 2^40
 // elements so that grid sizes fit in 32 bits.
@@ -40,7 +43,7 @@ extern "C" {
 
 size_t fp8_linear_workspace_bytes(int64_t rows, int64_t cols, int scaling) {
   if (bad_dim(rows) || bad_dim(cols)) return 0;
-  if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return 0;
+  if (bad_scaling(scaling)) return 0;
   return fp8l::quantize_workspace_bytes(rows, cols, scaling);
 }
 
@@ -48,12 +51,12 @@ int fp8_linear_quantize(const void *x, int64_t rows, int64_t cols, int scaling,
                         void *q, void *qt, float *scale, float *scale_t,
                         float *amax_out, void *workspace, size_t workspace_bytes,
                         void *stream) {
-  if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return FP8L_EINVAL;
+  if (bad_scaling(scaling)) return FP8L_EINVAL;
   if (bad_dim(rows) || bad_dim(cols) || rows * cols > kMaxElems) return FP8L_ESHAPE;
   const bool empty = rows == 0 || cols == 0;
   // scale vectors may be NULL only where they have no entries (rowwise, 0 rows
   // or 0 columns); tensorwise scales always have one entry
-  const bool rw = scaling == FP8L_ROWWISE;
+  const bool rw = (scaling & FP8L_ROWWISE) != 0;
   if ((!scale && (!rw || rows > 0)) || (!scale_t && (!rw || cols > 0))) return FP8L_EINVAL;
   if (!empty && (!x || !q || !qt)) return FP8L_EINVAL;
   const size_t need = fp8l::quantize_workspace_bytes(rows, cols, scaling);
@@ -80,7 +83,7 @@ int fp8_linear_fwd(const void *xq, const float *sx, const void *wq,
   if (s != FP8L_OK) return s;
   const int vec = scaling == FP8L_ROWWISE;
   hipError_t e = fp8l::gemm_launch(static_cast<const uint8_t *>(xq), sx,
-                                   static_cast<const uint8_t *>(wq), sw, vec, M, N, K,
+                                   static_cast<const uint8_t *>(wq), sw, vec, 0, M, N, K,
                                    static_cast<uint16_t *>(out),
                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
@@ -91,7 +94,7 @@ int fp8_linear_bwd(const void *dyq, const float *sdy, const void *dytq,
                    const void *xtq, const float *sxt, int64_t M, int64_t N,
                    int64_t K, int scaling, void *grad_x, void *grad_w,
                    void *stream) {
-  if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return FP8L_EINVAL;
+  if (bad_scaling(scaling)) return FP8L_EINVAL;
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8L_ESHAPE;
   // grad_x: [M,K] from [M,N] x [K,N]; grad_w: [N,K] from [N,M] x [K,M]
   if (bad_gemm_sizes(M, K, N) || bad_gemm_sizes(N, K, M)) return FP8L_ESHAPE;
@@ -101,16 +104,17 @@ int fp8_linear_bwd(const void *dyq, const float *sdy, const void *dytq,
     return s;
   if (grad_w && (s = check_gemm_operands(dytq, sdyt, xtq, sxt, grad_w, N, K, M)) != FP8L_OK)
     return s;
-  const int vec = scaling == FP8L_ROWWISE;
+  const int vec = (scaling & FP8L_ROWWISE) != 0;
+  const int fa = (scaling & FP8L_E5M2) != 0;     // dY operands in E5M2
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (grad_x)  // [M,K] = dYq[M,N] . WTq[K,N]^T
     e = fp8l::gemm_launch(static_cast<const uint8_t *>(dyq), sdy,
-                          static_cast<const uint8_t *>(wtq), swt, vec, M, K, N,
+                          static_cast<const uint8_t *>(wtq), swt, vec, fa, M, K, N,
                           static_cast<uint16_t *>(grad_x), st);
   if (e == hipSuccess && grad_w)  // [N,K] = dYTq[N,M] . XTq[K,M]^T
     e = fp8l::gemm_launch(static_cast<const uint8_t *>(dytq), sdyt,
-                          static_cast<const uint8_t *>(xtq), sxt, vec, N, K, M,
+                          static_cast<const uint8_t *>(xtq), sxt, vec, fa, N, K, M,
                           static_cast<uint16_t *>(grad_w), st);
   return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
 }
@@ -145,7 +149,7 @@ int fp8_linear_quantize_scaled(const void *x, int64_t rows, int64_t cols, const 
 int fp8_linear_bwd_w_f32(const void *dytq, const float *sdyt, const void *xtq,
                          const float *sxt, int64_t M, int64_t N, int64_t K, int scaling,
                          float *grad_w, void *stream) {
-  if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return FP8L_EINVAL;
+  if (bad_scaling(scaling)) return FP8L_EINVAL;
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8L_ESHAPE;
   // [N,K] fp32 = dYTq[N,M] . XTq[K,M]^T: 4-byte outputs under the same
   // 32-bit offset limit
@@ -154,7 +158,8 @@ int fp8_linear_bwd_w_f32(const void *dytq, const float *sdyt, const void *xtq,
   if (s != FP8L_OK) return s;
   hipError_t e = fp8l::gemm_f32_launch(static_cast<const uint8_t *>(dytq), sdyt,
                                        static_cast<const uint8_t *>(xtq), sxt,
-                                       scaling == FP8L_ROWWISE, N, K, M, grad_w,
+                                       (scaling & FP8L_ROWWISE) != 0,
+                                       (scaling & FP8L_E5M2) != 0, N, K, M, grad_w,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
 }
@@ -164,7 +169,16 @@ int fp8_linear_encode_e4m3(const float *in, uint8_t *out, int64_t n, void *strea
   if (n == 0) return FP8L_OK;
   if (!in || !out) return FP8L_EINVAL;
   if (misaligned(in) || misaligned(out)) return FP8L_EALIGN;
-  hipError_t e = fp8l::encode_launch(in, out, n, static_cast<hipStream_t>(stream));
+  hipError_t e = fp8l::encode_launch(in, out, n, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
+int fp8_linear_encode_e5m2(const float *in, uint8_t *out, int64_t n, void *stream) {
+  if (n < 0 || n > kMaxElems) return FP8L_ESHAPE;
+  if (n == 0) return FP8L_OK;
+  if (!in || !out) return FP8L_EINVAL;
+  if (misaligned(in) || misaligned(out)) return FP8L_EALIGN;
+  hipError_t e = fp8l::encode_launch(in, out, n, 1, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
 }
 

@@ -31,12 +31,33 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
-// Scale from an amax given as |bf16| bits: s = 448 / max(a, 1e-12) as one
-// IEEE fp32 division (HIP's default fp32 divide is correctly rounded).  A
-// NaN amax compares false and yields NaN.
+// Saturating round-to-nearest-even E5M2 codes (gradients): magnitudes
+// >= 57344 clamp to 57344 (so +-inf too) before the hardware conversion;
+// NaN bypasses the clamp.
+__device__ __forceinline__ float sat57344(float v) {
+  float c = __builtin_amdgcn_fmed3f(v, -FP8L_E5M2_MAX, FP8L_E5M2_MAX);
+  return (v != v) ? v : c;
+}
+
+__device__ __forceinline__ uint32_t e5m2x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_bf8_f32(sat57344(a), sat57344(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_bf8_f32(sat57344(c), sat57344(d), w, true);
+  return (uint32_t)w;
+}
+
+// Code format of a quantized operand: 0 = E4M3, 1 = E5M2.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  return FMT ? e5m2x4(a, b, c, d) : e4m3x4(a, b, c, d);
+}
+
+// Scale from an amax: s = fmax / max(a, 1e-12) as one IEEE fp32 division
+// (HIP's default fp32 divide is correctly rounded), fmax = 448 (E4M3) or
+// 57344 (E5M2).  A NaN amax compares false and yields NaN.
+template <int FMT = 0>
 __device__ __forceinline__ float scale_from_amax(float a) {
   float d = (a < FP8L_AMAX_EPS) ? FP8L_AMAX_EPS : a;
-  return FP8L_E4M3_MAX / d;
+  return (FMT ? FP8L_E5M2_MAX : FP8L_E4M3_MAX) / d;
 }
 
 // ---------------------------------------------------------- host launchers --
@@ -48,7 +69,7 @@ hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
                            int scaling, void *q, void *qt, float *scale,
                            float *scale_t, float *amax_out, void *workspace,
                            hipStream_t stream);
-hipError_t encode_launch(const float *in, uint8_t *out, int64_t n,
+hipError_t encode_launch(const float *in, uint8_t *out, int64_t n, int fmt,
                          hipStream_t stream);
 // Tensorwise amax of x into amax_out[0] (workspace: the tensorwise quantize
 // workspace of the same shape).
@@ -60,12 +81,13 @@ hipError_t quantize_scaled_launch(const void *x, int64_t rows, int64_t cols,
 
 // C[M,N] (bf16) = (A[M,K] . B[N,K]^T) * (1/sa) * (1/sb); with rowwise, sa
 // has M entries and sb N entries, else one each.
+// fmt_a: code format of A (0 = E4M3, 1 = E5M2); B is E4M3.
 hipError_t gemm_launch(const uint8_t *A, const float *sa, const uint8_t *B,
-                       const float *sb, int rowwise, int64_t M, int64_t N,
+                       const float *sb, int rowwise, int fmt_a, int64_t M, int64_t N,
                        int64_t K, uint16_t *C, hipStream_t stream);
 // The same GEMM with fp32 output: C32[M,N] = fl32(fl32(acc / sa) / sb).
 hipError_t gemm_f32_launch(const uint8_t *A, const float *sa, const uint8_t *B,
-                           const float *sb, int rowwise, int64_t M, int64_t N,
+                           const float *sb, int rowwise, int fmt_a, int64_t M, int64_t N,
                            int64_t K, float *C, hipStream_t stream);
 
 }  // namespace fp8l

@@ -146,8 +146,11 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m,
 
 // KFULL: K % 128 == 0 (no K tail, no per-chunk K check).  RW: rowwise
 // scales (sa[M], sb[N]) instead of one scale per operand.  F32: fp32 output
-// (the scaled value before bf16 rounding) instead of bf16.
-template <bool KFULL, bool RW, bool F32>
+// (the scaled value before bf16 rounding) instead of bf16.  FA: code format
+// of A (0 = E4M3, 1 = E5M2 gradients); B is E4M3.  The instruction's
+// format selectors apply to its first and second source operand, here the
+// B and the A fragment.
+template <bool KFULL, bool RW, bool F32, int FA>
 __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
     const uint8_t *__restrict__ A, const float *__restrict__ sa,
     const uint8_t *__restrict__ B, const float *__restrict__ sb,
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
   } while (0)
 #define FP8L_MF(J, I)                                                             \
   acc[J][I] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                   \
-      fb[J], fa[I], acc[J][I], 0, 0, 0, 0, 0, 0)
+      fb[J], fa[I], acc[J][I], 0, FA, 0, 0, 0, 0)
   // slot S (0..31) of a half runs MFMA (B frag S/4) x (A frag I0 + S%4)
   // plus the memory instructions listed for it
 #define FP8L_M(S, I0) FP8L_MF((S) / 4, (I0) + (S) % 4);
@@ -501,34 +504,40 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
 
 }  // namespace
 
-hipError_t gemm_launch(const uint8_t *A, const float *sa, const uint8_t *B,
-                       const float *sb, int rowwise, int64_t M, int64_t N,
-                       int64_t K, uint16_t *C, hipStream_t stream) {
+namespace {
+
+template <bool F32, int FA>
+hipError_t launch_variant(const uint8_t *A, const float *sa, const uint8_t *B,
+                          const float *sb, int rowwise, int64_t M, int64_t N, int64_t K,
+                          void *C, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   const bool kfull = K % BK == 0;
-  auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true, false> : k_gemm_fp8_tn<false, true, false>)
-                      : (kfull ? k_gemm_fp8_tn<true, false, false> : k_gemm_fp8_tn<false, false, false>);
+  auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true, F32, FA>
+                               : k_gemm_fp8_tn<false, true, F32, FA>)
+                      : (kfull ? k_gemm_fp8_tn<true, false, F32, FA>
+                               : k_gemm_fp8_tn<false, false, F32, FA>);
   hipLaunchKernelGGL(kern, grid, dim3(THREADS), 0, stream, A, sa, B, sb, (int)M, (int)N,
-                     (int)K, (void *)C, tiles_m, tiles_n);
+                     (int)K, C, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t gemm_launch(const uint8_t *A, const float *sa, const uint8_t *B,
+                       const float *sb, int rowwise, int fmt_a, int64_t M, int64_t N,
+                       int64_t K, uint16_t *C, hipStream_t stream) {
+  return fmt_a ? launch_variant<false, 1>(A, sa, B, sb, rowwise, M, N, K, C, stream)
+               : launch_variant<false, 0>(A, sa, B, sb, rowwise, M, N, K, C, stream);
+}
+
 hipError_t gemm_f32_launch(const uint8_t *A, const float *sa, const uint8_t *B,
-                           const float *sb, int rowwise, int64_t M, int64_t N,
+                           const float *sb, int rowwise, int fmt_a, int64_t M, int64_t N,
                            int64_t K, float *C, hipStream_t stream) {
-  if (M == 0 || N == 0) return hipSuccess;
-  const int tiles_m = (int)((M + BM - 1) / BM);
-  const int tiles_n = (int)((N + BN - 1) / BN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
-  const bool kfull = K % BK == 0;
-  auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true, true> : k_gemm_fp8_tn<false, true, true>)
-                      : (kfull ? k_gemm_fp8_tn<true, false, true> : k_gemm_fp8_tn<false, false, true>);
-  hipLaunchKernelGGL(kern, grid, dim3(THREADS), 0, stream, A, sa, B, sb, (int)M, (int)N,
-                     (int)K, (void *)C, tiles_m, tiles_n);
-  return hipGetLastError();
+  return fmt_a ? launch_variant<true, 1>(A, sa, B, sb, rowwise, M, N, K, C, stream)
+               : launch_variant<true, 0>(A, sa, B, sb, rowwise, M, N, K, C, stream);
 }
 
 }  // namespace fp8l

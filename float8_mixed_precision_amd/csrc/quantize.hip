@@ -149,10 +149,11 @@ __global__ __launch_bounds__(AM_THREADS) void k_amax_finish(
 }
 
 // Empty tensor: the scale of amax 0.
+template <int FMT>
 __global__ __launch_bounds__(64) void k_finalize_tw_empty(float *scale, float *scale_t,
                                                           float *amax_out) {
   if (threadIdx.x == 0) {
-    const float sc = scale_from_amax(0.f);
+    const float sc = scale_from_amax<FMT>(0.f);
     scale[0] = sc;
     scale_t[0] = sc;
     if (amax_out) amax_out[0] = 0.f;
@@ -219,6 +220,7 @@ __global__ __launch_bounds__(AM_THREADS) void k_amax_partial(
 // ------------------------------------------------------------- finalize --
 
 // one thread per output: rows first (max over tiles_c partials), then columns
+template <int FMT>
 __global__ __launch_bounds__(256) void k_finalize_rowwise(
     const uint16_t *__restrict__ rowpart, const uint16_t *__restrict__ colpart,
     int rows, int cols, int tiles_c, int tiles_r, float *scale, float *scale_t,
@@ -228,14 +230,14 @@ __global__ __launch_bounds__(256) void k_finalize_rowwise(
     uint32_t m = 0;
     for (int t = 0; t < tiles_c; ++t) m = max(m, (uint32_t)rowpart[(size_t)t * rows + i]);
     const float a = bf16_to_f32(m);
-    scale[i] = scale_from_amax(a);
+    scale[i] = scale_from_amax<FMT>(a);
     if (amax_out) amax_out[i] = a;
   } else if (i < rows + cols) {
     const int c = i - rows;
     uint32_t m = 0;
     for (int t = 0; t < tiles_r; ++t) m = max(m, (uint32_t)colpart[(size_t)t * cols + c]);
     const float a = bf16_to_f32(m);
-    scale_t[c] = scale_from_amax(a);
+    scale_t[c] = scale_from_amax<FMT>(a);
     if (amax_out) amax_out[rows + c] = a;
   }
 }
@@ -261,8 +263,9 @@ __global__ __launch_bounds__(256) void k_finalize_rowwise(
 // tensor's scale; block 0 also stores it (scale, scale_t, amax_out).
 // MODE_RW: scale / scale_t are inputs (from k_finalize_rowwise).
 // MODE_GIVEN: scale[0] is a tensorwise multiplier given by the caller.
+// FMT: 0 = E4M3 codes, 1 = E5M2 codes (scale onto 57344).
 constexpr int MODE_TW = 0, MODE_RW = 1, MODE_GIVEN = 2;
-template <int MODE>
+template <int MODE, int FMT>
 __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
     const uint16_t *__restrict__ x, int rows, int cols, int tiles_c,
     float *__restrict__ scale, float *__restrict__ scale_t,
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
     __shared__ uint32_t red[CT_THREADS / 64];
     const uint32_t am = tw_amax_bits(part, nparts, red);
     const float a = bf16_to_f32(am);
-    s_t = scale_from_amax(a);
+    s_t = scale_from_amax<FMT>(a);
     if (blockIdx.x == 0 && tid == 0) {
       scale[0] = s_t;
       scale_t[0] = s_t;
@@ -316,12 +319,12 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
         f[4] = bf16_to_f32(v.z & 0xFFFFu); f[5] = bf16_to_f32(v.z >> 16);
         f[6] = bf16_to_f32(v.w & 0xFFFFu); f[7] = bf16_to_f32(v.w >> 16);
         const float s = ROWWISE ? scale[r + j] : s_t;
-        const uint32_t q0 = e4m3x4(f[0] * s, f[1] * s, f[2] * s, f[3] * s);
-        const uint32_t q1 = e4m3x4(f[4] * s, f[5] * s, f[6] * s, f[7] * s);
+        const uint32_t q0 = fp8x4<FMT>(f[0] * s, f[1] * s, f[2] * s, f[3] * s);
+        const uint32_t q1 = fp8x4<FMT>(f[4] * s, f[5] * s, f[6] * s, f[7] * s);
         *reinterpret_cast<uint2 *>(q + (size_t)(r + j) * cols + c) = make_uint2(q0, q1);
         if (ROWWISE) {
-          lo[j] = e4m3x4(f[0] * sc[0], f[1] * sc[1], f[2] * sc[2], f[3] * sc[3]);
-          hi[j] = e4m3x4(f[4] * sc[4], f[5] * sc[5], f[6] * sc[6], f[7] * sc[7]);
+          lo[j] = fp8x4<FMT>(f[0] * sc[0], f[1] * sc[1], f[2] * sc[2], f[3] * sc[3]);
+          hi[j] = fp8x4<FMT>(f[4] * sc[4], f[5] * sc[5], f[6] * sc[6], f[7] * sc[7]);
         } else {
           lo[j] = q0;
           hi[j] = q1;
@@ -369,6 +372,7 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
 
 // --------------------------------------------------------------- encode --
 
+template <int FMT>
 __global__ __launch_bounds__(256) void k_encode(const float *__restrict__ in,
                                                 uint8_t *__restrict__ out,
                                                 int64_t n) {
@@ -376,11 +380,11 @@ __global__ __launch_bounds__(256) void k_encode(const float *__restrict__ in,
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
     const float4 v = reinterpret_cast<const float4 *>(in)[i];
-    reinterpret_cast<uint32_t *>(out)[i] = e4m3x4(v.x, v.y, v.z, v.w);
+    reinterpret_cast<uint32_t *>(out)[i] = fp8x4<FMT>(v.x, v.y, v.z, v.w);
   }
   // tail (n not a multiple of 4)
   const int64_t t = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < n && t < n4 * 4 + 4) out[t] = (uint8_t)(e4m3x4(in[t], 0.f, 0.f, 0.f) & 0xFFu);
+  if (t < n && t < n4 * 4 + 4) out[t] = (uint8_t)(fp8x4<FMT>(in[t], 0.f, 0.f, 0.f) & 0xFFu);
 }
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -403,7 +407,7 @@ int64_t tw_blocks(int64_t rows, int64_t cols) {
 size_t quantize_workspace_bytes(int64_t rows, int64_t cols, int scaling) {
   const AmaxGeom g = amax_geom(rows, cols);
   size_t bytes;
-  if (scaling == FP8L_TENSORWISE) {
+  if (!(scaling & FP8L_ROWWISE)) {
     bytes = (size_t)tw_blocks(rows, cols) * sizeof(uint32_t);
   } else {
     bytes = (size_t)(g.tiles_c * rows + g.tiles_r * cols) * sizeof(uint16_t) + 256;
@@ -411,26 +415,27 @@ size_t quantize_workspace_bytes(int64_t rows, int64_t cols, int scaling) {
   return (bytes + 255) & ~(size_t)255;
 }
 
-hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
-                           int scaling, void *q, void *qt, float *scale,
-                           float *scale_t, float *amax_out, void *workspace,
-                           hipStream_t stream) {
+namespace {
+
+template <int FMT>
+hipError_t quantize_launch_fmt(const void *x, int64_t rows, int64_t cols, bool rowwise,
+                               void *q, void *qt, float *scale, float *scale_t,
+                               float *amax_out, void *workspace, hipStream_t stream) {
   const AmaxGeom g = amax_geom(rows, cols);
   const int64_t ntiles = g.tiles_r * g.tiles_c;
   const uint16_t *xb = static_cast<const uint16_t *>(x);
-  uint16_t *ws = static_cast<uint16_t *>(workspace);
   const int R = (int)rows, C = (int)cols;
-  const int64_t nb = scaling == FP8L_TENSORWISE ? tw_blocks(rows, cols) : 0;
+  const int64_t nb = rowwise ? 0 : tw_blocks(rows, cols);
   uint32_t *part = static_cast<uint32_t *>(workspace);
-  if (scaling == FP8L_TENSORWISE) {
+  if (!rowwise) {
     if (nb > 0)
       hipLaunchKernelGGL(k_amax_tw, dim3((unsigned)nb), dim3(AM_THREADS), 0, stream,
                          static_cast<const uint4 *>(x), rows * cols / 8, part);
     else
-      hipLaunchKernelGGL(k_finalize_tw_empty, dim3(1), dim3(64), 0, stream, scale, scale_t,
-                         amax_out);
+      hipLaunchKernelGGL(k_finalize_tw_empty<FMT>, dim3(1), dim3(64), 0, stream, scale,
+                         scale_t, amax_out);
   } else {
-    uint16_t *rowpart = ws;
+    uint16_t *rowpart = static_cast<uint16_t *>(workspace);
     // column partials start on a 256-byte boundary after the row partials
     size_t off = ((size_t)(g.tiles_c * rows) * sizeof(uint16_t) + 255) & ~(size_t)255;
     uint16_t *colpart = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(workspace) + off);
@@ -438,26 +443,40 @@ hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
       hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)ntiles), dim3(AM_THREADS), 0,
                          stream, xb, R, C, (int)g.tiles_c, rowpart, colpart);
     if (rows + cols > 0)
-      hipLaunchKernelGGL(k_finalize_rowwise, dim3((unsigned)cdiv(rows + cols, 256)), dim3(256),
-                         0, stream, rowpart, colpart, R, C, (int)g.tiles_c, (int)g.tiles_r,
-                         scale, scale_t, amax_out);
+      hipLaunchKernelGGL(k_finalize_rowwise<FMT>, dim3((unsigned)cdiv(rows + cols, 256)),
+                         dim3(256), 0, stream, rowpart, colpart, R, C, (int)g.tiles_c,
+                         (int)g.tiles_r, scale, scale_t, amax_out);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t ct_r = cdiv(rows, CT_T), ct_c = cdiv(cols, CT_T);
   if (ct_r * ct_c > 0) {
-    if (scaling == FP8L_TENSORWISE)
-      hipLaunchKernelGGL(k_cast_transpose<MODE_TW>, dim3((unsigned)(ct_r * ct_c)),
+    if (!rowwise)
+      hipLaunchKernelGGL((k_cast_transpose<MODE_TW, FMT>), dim3((unsigned)(ct_r * ct_c)),
                          dim3(CT_THREADS), 0, stream, xb, R, C, (int)ct_c, scale, scale_t,
                          part, (int)nb, amax_out, static_cast<uint8_t *>(q),
                          static_cast<uint8_t *>(qt));
     else
-      hipLaunchKernelGGL(k_cast_transpose<MODE_RW>, dim3((unsigned)(ct_r * ct_c)),
+      hipLaunchKernelGGL((k_cast_transpose<MODE_RW, FMT>), dim3((unsigned)(ct_r * ct_c)),
                          dim3(CT_THREADS), 0, stream, xb, R, C, (int)ct_c, scale, scale_t,
                          nullptr, 0, nullptr, static_cast<uint8_t *>(q),
                          static_cast<uint8_t *>(qt));
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
+                           int scaling, void *q, void *qt, float *scale,
+                           float *scale_t, float *amax_out, void *workspace,
+                           hipStream_t stream) {
+  const bool rw = (scaling & FP8L_ROWWISE) != 0;
+  if (scaling & FP8L_E5M2)
+    return quantize_launch_fmt<1>(x, rows, cols, rw, q, qt, scale, scale_t, amax_out,
+                                  workspace, stream);
+  return quantize_launch_fmt<0>(x, rows, cols, rw, q, qt, scale, scale_t, amax_out,
+                                workspace, stream);
 }
 
 hipError_t amax_launch(const void *x, int64_t rows, int64_t cols, float *amax_out,
@@ -476,18 +495,22 @@ hipError_t quantize_scaled_launch(const void *x, int64_t rows, int64_t cols,
                                   const float *scale, void *q, void *qt, hipStream_t stream) {
   const int64_t ct_r = cdiv(rows, CT_T), ct_c = cdiv(cols, CT_T);
   if (ct_r * ct_c > 0)
-    hipLaunchKernelGGL(k_cast_transpose<MODE_GIVEN>, dim3((unsigned)(ct_r * ct_c)),
+    hipLaunchKernelGGL((k_cast_transpose<MODE_GIVEN, 0>), dim3((unsigned)(ct_r * ct_c)),
                        dim3(CT_THREADS), 0, stream, static_cast<const uint16_t *>(x), (int)rows,
                        (int)cols, (int)ct_c, const_cast<float *>(scale), nullptr, nullptr, 0,
                        nullptr, static_cast<uint8_t *>(q), static_cast<uint8_t *>(qt));
   return hipGetLastError();
 }
 
-hipError_t encode_launch(const float *in, uint8_t *out, int64_t n, hipStream_t stream) {
+hipError_t encode_launch(const float *in, uint8_t *out, int64_t n, int fmt,
+                         hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = cdiv(n / 4 + 1, 256);
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(k_encode, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n);
+  if (fmt)
+    hipLaunchKernelGGL(k_encode<1>, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n);
+  else
+    hipLaunchKernelGGL(k_encode<0>, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n);
   return hipGetLastError();
 }
 

@@ -21,11 +21,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_lib", "libfp8linear.so")
 
 FP8L_OK, FP8L_EINVAL, FP8L_ESHAPE, FP8L_EALIGN, FP8L_EWORKSPACE, FP8L_EHIP = range(6)
-FP8L_TENSORWISE, FP8L_ROWWISE = 0, 1
+FP8L_TENSORWISE, FP8L_ROWWISE, FP8L_E5M2 = 0, 1, 2
 EXPORTS = ("fp8_linear_workspace_bytes", "fp8_linear_quantize", "fp8_linear_amax",
            "fp8_linear_quantize_scaled", "fp8_linear_fwd", "fp8_linear_bwd",
-           "fp8_linear_bwd_w_f32", "fp8_linear_encode_e4m3", "fp8_linear_status_string",
-           "fp8_linear_version")
+           "fp8_linear_bwd_w_f32", "fp8_linear_encode_e4m3", "fp8_linear_encode_e5m2",
+           "fp8_linear_status_string", "fp8_linear_version")
 
 
 class Fp8LinearError(RuntimeError):
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
     L.fp8_linear_bwd_w_f32.argtypes = [P, P, P, P, i64, i64, i64, I, P, P]
     L.fp8_linear_encode_e4m3.restype = I
     L.fp8_linear_encode_e4m3.argtypes = [P, P, i64, P]
+    L.fp8_linear_encode_e5m2.restype = I
+    L.fp8_linear_encode_e5m2.argtypes = [P, P, i64, P]
     L.fp8_linear_status_string.restype = ctypes.c_char_p
     L.fp8_linear_status_string.argtypes = [I]
     L.fp8_linear_version.restype = ctypes.c_char_p
@@ -89,8 +91,8 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _scaling(rowwise: bool) -> int:
-    return FP8L_ROWWISE if rowwise else FP8L_TENSORWISE
+def _scaling(rowwise: bool, e5m2: bool = False) -> int:
+    return (FP8L_ROWWISE if rowwise else FP8L_TENSORWISE) | (FP8L_E5M2 if e5m2 else 0)
 
 
 # ----------------------------------------------------------- entry points --
@@ -126,8 +128,9 @@ def alloc_workspace(rows: int, cols: int, rowwise: bool, device) -> torch.Tensor
 def fp8_linear_quantize(x: torch.Tensor, rowwise: bool = False,
                         out: Optional[Quantized] = None,
                         workspace: Optional[torch.Tensor] = None,
-                        stream=None) -> Quantized:
-    """Quantize bf16 x [rows, cols] -> (q, qt, scale, scale_t, amax)."""
+                        stream=None, e5m2: bool = False) -> Quantized:
+    """Quantize bf16 x [rows, cols] -> (q, qt, scale, scale_t, amax); E5M2
+    codes (scale onto 57344) when e5m2."""
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
     rows, cols = x.shape
     if out is None:
@@ -135,7 +138,7 @@ def fp8_linear_quantize(x: torch.Tensor, rowwise: bool = False,
     if workspace is None:
         workspace = alloc_workspace(rows, cols, rowwise, x.device)
     _check(lib().fp8_linear_quantize(
-        _p(x), rows, cols, _scaling(rowwise), _p(out.q), _p(out.qt), _p(out.scale),
+        _p(x), rows, cols, _scaling(rowwise, e5m2), _p(out.q), _p(out.qt), _p(out.scale),
         _p(out.scale_t), _p(out.amax), _p(workspace), workspace.numel(), _stream(stream)),
         "fp8_linear_quantize")
     return out
@@ -158,15 +161,17 @@ def fp8_linear_fwd(xq: torch.Tensor, sx: torch.Tensor, wq: torch.Tensor,
 def fp8_linear_bwd(dyq, sdy, dytq, sdyt, wtq, swt, xtq, sxt, M: int, N: int, K: int,
                    rowwise: bool = False, grad_x: Optional[torch.Tensor] = None,
                    grad_w: Optional[torch.Tensor] = None, want_x: bool = True,
-                   want_w: bool = True, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """grad_x [M, K] = dY . W and grad_w [N, K] = dY^T . X from the fp8 copies."""
+                   want_w: bool = True, stream=None,
+                   e5m2: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """grad_x [M, K] = dY . W and grad_w [N, K] = dY^T . X from the fp8 copies
+    (dY's copies in E5M2 when e5m2)."""
     dev = (dyq if dyq is not None else dytq).device
     if want_x and grad_x is None:
         grad_x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     if want_w and grad_w is None:
         grad_w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     _check(lib().fp8_linear_bwd(_p(dyq), _p(sdy), _p(dytq), _p(sdyt), _p(wtq), _p(swt),
-                                _p(xtq), _p(sxt), M, N, K, _scaling(rowwise),
+                                _p(xtq), _p(sxt), M, N, K, _scaling(rowwise, e5m2),
                                 _p(grad_x if want_x else None),
                                 _p(grad_w if want_w else None), _stream(stream)),
            "fp8_linear_bwd")
@@ -206,12 +211,12 @@ def fp8_linear_quantize_scaled(x: torch.Tensor, scale: torch.Tensor,
 
 def fp8_linear_bwd_w_f32(dytq, sdyt, xtq, sxt, M: int, N: int, K: int,
                          rowwise: bool = False, grad_w: Optional[torch.Tensor] = None,
-                         stream=None) -> torch.Tensor:
+                         stream=None, e5m2: bool = False) -> torch.Tensor:
     """grad_w [N, K] fp32 = dY^T . X from the fp8 copies (no bf16 rounding)."""
     if grad_w is None:
         grad_w = torch.empty((N, K), dtype=torch.float32, device=dytq.device)
     _check(lib().fp8_linear_bwd_w_f32(_p(dytq), _p(sdyt), _p(xtq), _p(sxt), M, N, K,
-                                      _scaling(rowwise), _p(grad_w), _stream(stream)),
+                                      _scaling(rowwise, e5m2), _p(grad_w), _stream(stream)),
            "fp8_linear_bwd_w_f32")
     return grad_w
 
@@ -227,6 +232,17 @@ def fp8_linear_encode_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None,
     return out
 
 
+def fp8_linear_encode_e5m2(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """Device E5M2 saturating RNE codes of fp32 values."""
+    assert x.dtype == torch.float32 and x.is_contiguous()
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib().fp8_linear_encode_e5m2(_p(x), _p(out), x.numel(), _stream(stream)),
+           "fp8_linear_encode_e5m2")
+    return out
+
+
 def fp8_linear_version() -> str:
     return lib().fp8_linear_version().decode()
 
@@ -238,12 +254,14 @@ class LinearStep:
 
     Holds the bf16 inputs X [M, K], W [N, K], dY [M, N] and every output; a
     call to ``run()`` enqueues quantize(X), quantize(W), quantize(dY), the
-    forward GEMM and both backward GEMMs on the current stream.
+    forward GEMM and both backward GEMMs on the current stream.  With
+    ``e5m2_grad`` dY is quantized to E5M2 and the backward GEMMs read it so.
     """
 
     def __init__(self, x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor,
-                 rowwise: bool = False):
+                 rowwise: bool = False, e5m2_grad: bool = False):
         self.x, self.w, self.dy, self.rowwise = x, w, dy, rowwise
+        self.e5m2_grad = e5m2_grad
         self.M, self.K = x.shape
         self.N = w.shape[0]
         dev = x.device
@@ -261,7 +279,8 @@ class LinearStep:
     def quantize(self, stream=None):
         fp8_linear_quantize(self.x, self.rowwise, self.qx, self.ws, stream)
         fp8_linear_quantize(self.w, self.rowwise, self.qw, self.ws, stream)
-        fp8_linear_quantize(self.dy, self.rowwise, self.qdy, self.ws, stream)
+        fp8_linear_quantize(self.dy, self.rowwise, self.qdy, self.ws, stream,
+                            e5m2=self.e5m2_grad)
 
     def gemms(self, stream=None):
         fp8_linear_fwd(self.qx.q, self.qx.scale, self.qw.q, self.qw.scale, self.rowwise,
@@ -269,7 +288,7 @@ class LinearStep:
         fp8_linear_bwd(self.qdy.q, self.qdy.scale, self.qdy.qt, self.qdy.scale_t,
                        self.qw.qt, self.qw.scale_t, self.qx.qt, self.qx.scale_t,
                        self.M, self.N, self.K, self.rowwise, self.grad_x, self.grad_w,
-                       stream=stream)
+                       stream=stream, e5m2=self.e5m2_grad)
 
     def run(self, stream=None):
         self.quantize(stream)

@@ -67,9 +67,18 @@ extern "C" {
 #define FP8L_TENSORWISE  0   /* one scale per tensor                          */
 #define FP8L_ROWWISE     1   /* one scale per row of q, one per column of x
                                 (i.e. per row of qt)                         */
+/* Format flag, OR'ed into a `scaling` argument: E5M2 codes (the second FP8
+ * encoding the pages name, "torchtitan" tutorial, Part XI, item 9) for the
+ * gradient dY.  fp8_linear_quantize with it writes E5M2 q / qt whose scale
+ * maps amax onto 57344; fp8_linear_bwd and fp8_linear_bwd_w_f32 with it
+ * read dyq / dytq as E5M2 (the weight and activation operands stay E4M3).
+ * fp8_linear_fwd and fp8_linear_quantize_scaled take E4M3 only. */
+#define FP8L_E5M2        2
 
 /* Largest finite E4M3 value; the scale maps a tensor's amax onto it. */
 #define FP8L_E4M3_MAX    448.0f
+/* Largest finite E5M2 value (the gradient format, FP8L_E5M2 below). */
+#define FP8L_E5M2_MAX    57344.0f
 /* Lower clamp of amax in the scale, keeping the scale finite. */
 #define FP8L_AMAX_EPS    1e-12f
 
@@ -82,7 +91,9 @@ FP8L_API size_t fp8_linear_workspace_bytes(int64_t rows, int64_t cols, int scali
 
 /*
  * Quantize a bf16 matrix to E4M3 with dynamic scaling (amax of the current
- * tensor; the pages leave the recipe open, this is the reading taken):
+ * tensor; the pages leave the recipe open, this is the reading taken).
+ * With FP8L_E5M2 OR'ed into scaling, the codes are E5M2 and 448 below
+ * reads 57344:
  *
  *   a        = max |x| over the tensor (tensorwise), or per row of x for
  *              q and per column of x for qt (rowwise)
@@ -206,6 +217,11 @@ FP8L_API int fp8_linear_bwd_w_f32(const void *dytq, const float *sdyt, const voi
  */
 FP8L_API int fp8_linear_encode_e4m3(const float *in, uint8_t *out, int64_t n,
                            void *stream);
+
+/* The E5M2 counterpart (saturating at 57344, ties to even, NaN -> a NaN
+ * code), for testing the gradient conversion the same way. */
+FP8L_API int fp8_linear_encode_e5m2(const float *in, uint8_t *out, int64_t n,
+                                    void *stream);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 FP8L_API const char *fp8_linear_status_string(int status);

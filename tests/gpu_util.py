@@ -60,19 +60,21 @@ def assert_quantize_equal(got, ref, label=""):
                                  % (label, n, len(bad), i, int(g[i]), int(r[i])))
 
 
-def _abs_dot(a, b, tv, ii, jj, chunk=256):
+def _abs_dot(a, b, tv, ii, jj, chunk=256, tvb=None):
     """sum_t |A[i,t]| |B[j,t]| in float64 for the sampled pairs (codes are
-    decoded per chunk of samples, so full-size operands never expand)."""
-    av = np.abs(tv)
+    decoded per chunk of samples, so full-size operands never expand); tv
+    decodes A's codes and tvb (default tv) B's."""
+    av = np.abs(np.nan_to_num(tv, nan=0.0, posinf=0.0, neginf=0.0))
+    bv = av if tvb is None else np.abs(np.nan_to_num(tvb, nan=0.0, posinf=0.0, neginf=0.0))
     out = np.empty(len(ii), np.float64)
     for s in range(0, len(ii), chunk):
         x = av[a[ii[s:s + chunk]]]
-        y = av[b[jj[s:s + chunk]]]
+        y = bv[b[jj[s:s + chunk]]]
         out[s:s + chunk] = np.einsum("ij,ij->i", x, y)
     return out
 
 
-def gemm_parity(G, O, a, b, sa, sb, ii=None, jj=None, label="", frob_tol=1e-3):
+def gemm_parity(G, O, a, b, sa, sb, ii=None, jj=None, label="", frob_tol=1e-3, e5m2_a=False):
     """Compare GPU bf16 outputs G with the oracle's O (same fp8 inputs).
 
     Required: relative Frobenius <= frob_tol and, for every element,
@@ -92,7 +94,8 @@ def gemm_parity(G, O, a, b, sa, sb, ii=None, jj=None, label="", frob_tol=1e-3):
     inva = inva[ii] if inva.size > 1 else np.full(len(ii), inva[0])
     invb = invb[jj] if invb.size > 1 else np.full(len(jj), invb[0])
     tv = oracle.e4m3_values()
-    absdot = _abs_dot(a, b, tv, np.asarray(ii), np.asarray(jj))
+    ta = oracle.e5m2_values() if e5m2_a else tv
+    absdot = _abs_dot(a, b, ta, np.asarray(ii), np.asarray(jj), tvb=tv)
     g = oracle.bf16_to_f32(G).astype(np.float64)
     o = oracle.bf16_to_f32(O).astype(np.float64)
     nxt = oracle.bf16_to_f32((O & 0x7FFF) + 1).astype(np.float64)

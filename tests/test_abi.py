@@ -78,7 +78,8 @@ def q_call(x=A16, rows=16, cols=16, scaling=0, q=A16, qt=A16, s=A16, st=A16,
 @pytestmark_cpu
 def test_quantize_rejects_bad_arguments():
     E = ops
-    assert q_call(scaling=2) == E.FP8L_EINVAL
+    assert q_call(scaling=4) == E.FP8L_EINVAL               # unknown flag
+    assert q_call(scaling=-1) == E.FP8L_EINVAL
     assert q_call(rows=17) == E.FP8L_ESHAPE
     assert q_call(cols=-16) == E.FP8L_ESHAPE
     assert q_call(rows=1 << 31) == E.FP8L_ESHAPE
@@ -110,6 +111,7 @@ def test_gemm_entry_points_reject_bad_arguments():
                                 M, N, K, scaling, P(out) if out else None, None)
 
     assert fwd(scaling=-1) == E.FP8L_EINVAL
+    assert fwd(scaling=E.FP8L_E5M2) == E.FP8L_EINVAL       # the forward takes E4M3 only
     assert fwd(M=8) == E.FP8L_ESHAPE
     assert fwd(K=-16) == E.FP8L_ESHAPE
     assert fwd(xq=None) == E.FP8L_EINVAL
@@ -131,7 +133,7 @@ def test_gemm_entry_points_reject_bad_arguments():
     assert bwd() == E.FP8L_EALIGN                    # grad_x operands checked
     assert bwd(wtq=None) == E.FP8L_EINVAL
     assert bwd(gw=A_BAD, wtq=A16) == E.FP8L_EALIGN   # grad_w output checked
-    assert bwd(scaling=3) == E.FP8L_EINVAL
+    assert bwd(scaling=4) == E.FP8L_EINVAL
 
 
 @pytestmark_cpu
@@ -179,7 +181,7 @@ def test_amax_scaled_and_f32_entry_points_reject_bad_arguments():
                                       P(xt) if xt else None, P(sxt) if sxt else None,
                                       M, N, K, scaling, P(gw) if gw else None, None)
 
-    assert bw(scaling=3) == E.FP8L_EINVAL
+    assert bw(scaling=8) == E.FP8L_EINVAL
     assert bw(N=40) == E.FP8L_ESHAPE
     assert bw(N=32768, K=32768) == E.FP8L_ESHAPE        # 4 GiB of fp32 output
     assert bw(gw=None) == E.FP8L_EINVAL
