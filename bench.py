@@ -42,6 +42,8 @@ def parse():
                    help="skip the CPU oracle timing (e.g. under a profiler)")
     p.add_argument("--cpu-rows", type=int, default=128,
                    help="output rows per GEMM in the CPU oracle sample")
+    p.add_argument("--no-next-rows", action="store_true",
+                   help="skip the next_rows measurements (profiling runs of the step alone)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="only run 3 plain device copies of this many bytes (the "
                         "calibration kernel for HBM byte counters) and exit")
@@ -332,9 +334,10 @@ def main():
                                    "quantize": round(q_ms / args.steps, 4)},
         "cpu_baseline": None,
     }
-    print("[bench] next rows", file=sys.stderr, flush=True)
-    result["next_rows"] = measure_next_rows(steps, stream)
-    result["next_rows"]["e5m2_grad_step"] = measure_e5m2_step(steps, wl.flops)
+    if not args.no_next_rows:
+        print("[bench] next rows", file=sys.stderr, flush=True)
+        result["next_rows"] = measure_next_rows(steps, stream)
+        result["next_rows"]["e5m2_grad_step"] = measure_e5m2_step(steps, wl.flops)
     del steps, shared
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
