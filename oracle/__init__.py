@@ -81,6 +81,13 @@ class Oracle:
         lib.orc_gemm_tn_mixed_sampled.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P,
                                                   ctypes.c_int, P, ctypes.c_int, i64, P, P,
                                                   i64, P]
+        lib.orc_silu.restype = ctypes.c_float
+        lib.orc_silu.argtypes = [ctypes.c_float]
+        lib.orc_dsilu.restype = ctypes.c_float
+        lib.orc_dsilu.argtypes = [ctypes.c_float]
+        lib.orc_swiglu_fwd.argtypes = [P, P, i64, P]
+        lib.orc_swiglu_bwd.argtypes = [P, P, P, i64, P, P]
+        lib.orc_add_bf16.argtypes = [P, P, i64, P]
         lib.orc_amax.restype = ctypes.c_float
         lib.orc_amax.argtypes = [P, i64]
         lib.orc_quantize_scaled.argtypes = [P, i64, i64, ctypes.c_float, P, P]
@@ -183,6 +190,44 @@ class Oracle:
         self.lib.orc_quantize_e5m2(_ptr(x), rows, cols, int(bool(rowwise)), _ptr(q),
                                    _ptr(qt), _ptr(s), _ptr(st), _ptr(am))
         return q, qt, s, st, am
+
+    # ------------------------------------------------------------ SwiGLU --
+    def silu(self, a: float) -> np.float32:
+        return np.float32(self.lib.orc_silu(float(np.float32(a))))
+
+    def dsilu(self, a: float) -> np.float32:
+        return np.float32(self.lib.orc_dsilu(float(np.float32(a))))
+
+    def swiglu_fwd(self, a_bits, b_bits):
+        """h = bf16(fl32(fl32(silu(a)) * b)), elementwise (bf16 bits)."""
+        a = _c(a_bits, np.uint16)
+        b = _c(b_bits, np.uint16)
+        assert a.shape == b.shape
+        h = np.empty(a.shape, np.uint16)
+        self.lib.orc_swiglu_fwd(_ptr(a), _ptr(b), a.size, _ptr(h))
+        return h
+
+    def swiglu_bwd(self, dh_bits, a_bits, b_bits):
+        """(da, db) of h = silu(a) * b for the output gradient dh (bf16 bits):
+        da = bf16(fl32(fl32(dh * b) * fl32(silu'(a)))),
+        db = bf16(fl32(dh * fl32(silu(a))))."""
+        dh = _c(dh_bits, np.uint16)
+        a = _c(a_bits, np.uint16)
+        b = _c(b_bits, np.uint16)
+        assert a.shape == b.shape == dh.shape
+        da = np.empty(a.shape, np.uint16)
+        db = np.empty(a.shape, np.uint16)
+        self.lib.orc_swiglu_bwd(_ptr(dh), _ptr(a), _ptr(b), a.size, _ptr(da), _ptr(db))
+        return da, db
+
+    def add_bf16(self, x_bits, y_bits):
+        """bf16(fl32(x) + fl32(y)), elementwise (bf16 bits)."""
+        x = _c(x_bits, np.uint16)
+        y = _c(y_bits, np.uint16)
+        assert x.shape == y.shape
+        out = np.empty(x.shape, np.uint16)
+        self.lib.orc_add_bf16(_ptr(x), _ptr(y), x.size, _ptr(out))
+        return out
 
     def amax(self, x_bits) -> np.float32:
         """max |x| over a bf16 tensor (NaN-propagating; 0 for an empty one)."""
@@ -365,6 +410,18 @@ def gemm_tn_sampled(a, sa, b, sb, ii, jj, return_acc=False):
 
 def amax(x_bits):
     return default().amax(x_bits)
+
+
+def swiglu_fwd(a_bits, b_bits):
+    return default().swiglu_fwd(a_bits, b_bits)
+
+
+def swiglu_bwd(dh_bits, a_bits, b_bits):
+    return default().swiglu_bwd(dh_bits, a_bits, b_bits)
+
+
+def add_bf16(x_bits, y_bits):
+    return default().add_bf16(x_bits, y_bits)
 
 
 def e5m2_values():

@@ -25,6 +25,11 @@
  *   - The GEMMs accumulate products of decoded codes in fp32, in ascending
  *     order of the contraction index, and are dequantised by fp32
  *     reciprocals of the two scales and rounded to bf16 (ties to even).
+ *   - The feed-forward block the linears sit in is the Llama 3.1 MLP that
+ *     the tutorial page trains (Part II, "Using it", llama3_8b; Part V
+ *     splits its hidden dimension): SwiGLU, h = silu(x W1^T) * (x W3^T),
+ *     out = h W2^T.  Its elementwise part and the bf16 sum of the two
+ *     gradient contributions of x are at the end of this file.
  *
  * Nothing here is blocked, fused or reordered beyond these definitions.  The
  * only concession to speed is the OpenMP pragma on the outermost loops, which
@@ -497,4 +502,65 @@ void orc_gemm_tn_mixed_sampled(const uint8_t *a, int fmt_a, const float *sa, int
         out[s] = gemm_element_mixed(a + i * k, ta, b + j * k, tb, k,
                                     a_vec ? sa[i] : sa[0], b_vec ? sb[j] : sb[0]);
     }
+}
+
+/* ------------------------------------------------------------- SwiGLU -- */
+
+/* The SwiGLU feed-forward of the Llama 3.1 model the tutorial page trains:
+ *   h = silu(a) * b,  silu(a) = a * sigma(a) = a / (1 + e^-a)
+ * with a = x.W1^T and b = x.W3^T, each [rows, cols].  Reading: bf16 inputs
+ * are widened to fp32, silu is the fp32 rounding of its exact value, one
+ * fp32 product, one bf16 rounding:
+ *   h = bf16( fl32( fl32(silu(a)) * b ) )
+ * Backward, with the derivative silu'(a) = sigma(a) (1 + a (1 - sigma(a))):
+ *   da = bf16( fl32( fl32(dh * b) * fl32(silu'(a)) ) )
+ *   db = bf16( fl32( dh * fl32(silu(a)) ) )
+ * silu and silu' are evaluated in float64 and rounded once to fp32.       */
+float orc_silu(float a)
+{
+    double x = (double)a;
+    return (float)(x / (1.0 + exp(-x)));
+}
+
+float orc_dsilu(float a)
+{
+    double x = (double)a;
+    double sg = 1.0 / (1.0 + exp(-x));
+    return (float)(sg * (1.0 + x * (1.0 - sg)));
+}
+
+/* a, b, h: bf16 [n] (any shape, element by element) */
+void orc_swiglu_fwd(const uint16_t *a, const uint16_t *b, int64_t n, uint16_t *h)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        float av = orc_bf16_to_f32(a[i]);
+        float bv = orc_bf16_to_f32(b[i]);
+        h[i] = orc_f32_to_bf16(orc_silu(av) * bv);
+    }
+}
+
+/* dh, a, b, da, db: bf16 [n] */
+void orc_swiglu_bwd(const uint16_t *dh, const uint16_t *a, const uint16_t *b, int64_t n,
+                    uint16_t *da, uint16_t *db)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        float g = orc_bf16_to_f32(dh[i]);
+        float av = orc_bf16_to_f32(a[i]);
+        float bv = orc_bf16_to_f32(b[i]);
+        float gb = g * bv;
+        da[i] = orc_f32_to_bf16(gb * orc_dsilu(av));
+        db[i] = orc_f32_to_bf16(g * orc_silu(av));
+    }
+}
+
+/* x feeds two linears of the block (w1 and w3), so its gradient is the sum
+ * of their two bf16 grad_X outputs, added as bf16 tensors are: widened to
+ * fp32, one fp32 addition, one bf16 rounding. */
+void orc_add_bf16(const uint16_t *x, const uint16_t *y, int64_t n, uint16_t *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = orc_f32_to_bf16(orc_bf16_to_f32(x[i]) + orc_bf16_to_f32(y[i]));
 }

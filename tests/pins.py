@@ -598,10 +598,132 @@ def check_gemm_mixed(o, seed: int = 18) -> None:
     assert np.array_equal(o.gemm_tn_mixed_sampled(a5, 1, sa, b, 0, sb, ii, jj), out[ii, jj])
 
 
+# --------------------------------------------------------------- SwiGLU --
+
+def _all_finite_bf16() -> np.ndarray:
+    """Every finite bf16 bit pattern."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    return bits[(bits & 0x7F80) != 0x7F80]
+
+
+def _bf16_value64(bits) -> np.ndarray:
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _torch_silu_and_grad64(a64: np.ndarray):
+    """silu and its derivative in float64 by torch (F.silu and autograd)."""
+    t = torch.from_numpy(np.ascontiguousarray(a64, np.float64)).requires_grad_(True)
+    y = torch.nn.functional.silu(t)
+    y.sum().backward()
+    return y.detach().numpy(), t.grad.numpy()
+
+
+def check_silu(o, seed: int = 19) -> None:
+    """silu on every finite bf16 input: the fp32 rounding of scipy's
+    a * expit(a) and of torch's float64 F.silu; silu(0) = 0; silu(a) = a
+    for large a, -> -0 for very negative a; silu(a) - silu(-a) = a within
+    the two fp32 roundings; silu' equals torch's float64 autograd rounded to
+    fp32 and a central difference of scipy's silu to 1e-6."""
+    from scipy.special import expit
+    a = _bf16_value64(_all_finite_bf16())
+    a = a[np.abs(a) < 1e30]                       # keep the scipy product finite
+    got = np.array([o.silu(v) for v in a[::7]], np.float32)
+    want_sp = (a[::7] * expit(a[::7])).astype(np.float32)
+    ts, tg = _torch_silu_and_grad64(a[::7])
+    assert np.array_equal(got.view(np.uint32), want_sp.view(np.uint32)), "silu vs scipy"
+    assert np.array_equal(got.view(np.uint32), ts.astype(np.float32).view(np.uint32)), \
+        "silu vs torch"
+    assert o.silu(0.0) == 0.0 and o.silu(100.0) == np.float32(100.0)
+    assert o.silu(-1000.0) == 0.0 and np.signbit(o.silu(-1000.0))
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(2000) * 6).astype(np.float32)
+    odd = np.array([float(o.silu(v)) - float(o.silu(-v)) for v in x])
+    tol = 2 * np.spacing(np.abs(x)).astype(np.float64) + 1e-30
+    assert np.all(np.abs(odd - x) <= tol), "silu(a) - silu(-a) != a"
+    gd = np.array([o.dsilu(v) for v in a[::7]], np.float32)
+    assert np.array_equal(gd.view(np.uint32), tg.astype(np.float32).view(np.uint32)), \
+        "silu' vs torch autograd"
+    xs = x.astype(np.float64)
+    h = 1e-5 * np.maximum(1.0, np.abs(xs))
+    f = lambda v: v * expit(v)
+    fd = (f(xs + h) - f(xs - h)) / (2 * h)
+    gx = np.array([o.dsilu(v) for v in x], np.float64)
+    assert np.all(np.abs(gx - fd) <= 1e-6 * np.maximum(1.0, np.abs(fd))), "silu' vs difference"
+    assert o.dsilu(0.0) == 0.5 and o.dsilu(1000.0) == 1.0
+
+
+def check_swiglu_fwd(o, seed: int = 20) -> None:
+    """h against torch: float64 F.silu rounded to fp32, an fp32 product with
+    b, torch's bf16 rounding.  b = 1 gives bf16(silu(a)); b = 0 gives +-0;
+    large a gives torch's bf16 product a*b; the order of a and b matters."""
+    rng = np.random.default_rng(seed)
+    from float8_mixed_precision_amd import workloads as W
+    a = W.to_bf16_bits((rng.standard_normal((64, 96)) * 3).astype(np.float32))
+    b = W.to_bf16_bits(rng.standard_normal((64, 96)).astype(np.float32))
+    a[0, :4] = [0x0000, 0x8000, 0x7FC0, 0xFF80]                 # 0, -0, NaN, -inf
+    a[1, :3] = [0x7F80, 0x42C8, 0xC2C8]                         # inf, 100, -100
+    h = o.swiglu_fwd(a, b)
+    s64, _ = _torch_silu_and_grad64(_bf16_value64(a))
+    want = torch_bf16_bits(s64.astype(np.float32) * _bf16_value64(b).astype(np.float32))
+    nan = np.isnan(_bf16_value64(want))
+    assert np.array_equal(np.isnan(_bf16_value64(h)), nan)
+    assert np.array_equal(h[~nan], want[~nan]), "swiglu fwd vs torch"
+    one = np.full(a.shape, 0x3F80, np.uint16)
+    assert np.array_equal(o.swiglu_fwd(a, one)[~nan], torch_bf16_bits(s64.astype(np.float32))[~nan])
+    big = W.to_bf16_bits((rng.random((8, 16)) * 100 + 20).astype(np.float32))
+    prod = torch_bf16_bits(_bf16_value64(big).astype(np.float32) * _bf16_value64(b[:8, :16]).astype(np.float32))
+    assert np.array_equal(o.swiglu_fwd(big, b[:8, :16]), prod)
+    zero = np.zeros(a.shape, np.uint16)
+    fin = np.isfinite(_bf16_value64(a))
+    assert np.all((o.swiglu_fwd(a, zero)[fin] & 0x7FFF) == 0)
+    assert not np.array_equal(o.swiglu_fwd(b, a), h)
+
+
+def check_swiglu_bwd(o, seed: int = 21) -> None:
+    """da, db against torch autograd of F.silu(a) * b in float64: within one
+    bf16 ulp of the exact gradients, and bit-equal to the exact gradients'
+    factors combined in the stated fp32 order."""
+    from oracle import bf16_ulp_distance
+    from float8_mixed_precision_amd import workloads as W
+    rng = np.random.default_rng(seed)
+    shape = (48, 80)
+    a = W.to_bf16_bits((rng.standard_normal(shape) * 3).astype(np.float32))
+    b = W.to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    dh = W.to_bf16_bits((rng.standard_normal(shape) * 1e-2).astype(np.float32))
+    da, db = o.swiglu_bwd(dh, a, b)
+    ta = torch.from_numpy(_bf16_value64(a)).requires_grad_(True)
+    tb = torch.from_numpy(_bf16_value64(b)).requires_grad_(True)
+    (torch.nn.functional.silu(ta) * tb).backward(torch.from_numpy(_bf16_value64(dh)))
+    assert np.all(bf16_ulp_distance(da, torch_bf16_bits(ta.grad.numpy().astype(np.float32))) <= 1)
+    assert np.all(bf16_ulp_distance(db, torch_bf16_bits(tb.grad.numpy().astype(np.float32))) <= 1)
+    s64, g64 = _torch_silu_and_grad64(_bf16_value64(a))
+    dh32 = _bf16_value64(dh).astype(np.float32)
+    b32 = _bf16_value64(b).astype(np.float32)
+    assert np.array_equal(da, torch_bf16_bits((dh32 * b32) * g64.astype(np.float32)))
+    assert np.array_equal(db, torch_bf16_bits(dh32 * s64.astype(np.float32)))
+
+
+def check_add_bf16(o, seed: int = 22) -> None:
+    """bf16 + bf16 equals torch's CPU bf16 addition, finite and special."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(0, 1 << 16, 50000).astype(np.uint16)
+    y = rng.integers(0, 1 << 16, 50000).astype(np.uint16)
+    x[:6] = [0x7F80, 0xFF80, 0x7F80, 0x0001, 0x8000, 0x7F7F]
+    y[:6] = [0xFF80, 0x3F80, 0x7F80, 0x8001, 0x8000, 0x7F7F]
+    tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    ty = torch.from_numpy(y.view(np.int16)).view(torch.bfloat16)
+    want = (tx + ty).view(torch.int16).numpy().view(np.uint16)
+    got = o.add_bf16(x, y)
+    nan = np.isnan(_bf16_value64(want))
+    assert np.array_equal(np.isnan(_bf16_value64(got)), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
 ALL_CHECKS = [check_decode, check_encode_random, check_encode_brute_force,
               check_encode_invariants, check_bf16, check_scale,
               check_quantize_vs_library, check_quantize_invariants,
               check_gemm_vs_exact, check_gemm_exact_cases, check_gemm_scales,
               check_gemm_tiny_brute_force, check_gemm_sampled, check_amax,
               check_quantize_scaled, check_gemm_f32, check_e5m2_decode,
-              check_e5m2_encode, check_quantize_e5m2, check_gemm_mixed]
+              check_e5m2_encode, check_quantize_e5m2, check_gemm_mixed, check_silu,
+              check_swiglu_fwd, check_swiglu_bwd, check_add_bf16]

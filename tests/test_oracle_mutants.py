@@ -60,6 +60,21 @@ MUTANTS = {
     "gemm_mixed_table": ("sum += ta[arow[t]] * tb[brow[t]];", "sum += ta[arow[t]] * ta[brow[t]];"),
     # fp32 GEMM: output stored transposed
     "gemm_f32_store": ("out[i * n + j] = gemm_element_f32(", "out[j * m + i] = gemm_element_f32("),
+    # silu: wrong sign in the exponent
+    "silu_exp_sign": ("return (float)(x / (1.0 + exp(-x)));", "return (float)(x / (1.0 + exp(x)));"),
+    # silu': the (1 - sigma) factor dropped
+    "dsilu_term": ("return (float)(sg * (1.0 + x * (1.0 - sg)));", "return (float)(sg * (1.0 + x));"),
+    # SwiGLU forward: gate and value swapped
+    "swiglu_swap": ("h[i] = orc_f32_to_bf16(orc_silu(av) * bv);",
+                    "h[i] = orc_f32_to_bf16(orc_silu(bv) * av);"),
+    # SwiGLU backward: the b factor of da dropped
+    "swiglu_da_no_b": ("float gb = g * bv;", "float gb = g;"),
+    # SwiGLU backward: db takes silu' instead of silu
+    "swiglu_db_deriv": ("db[i] = orc_f32_to_bf16(g * orc_silu(av));",
+                        "db[i] = orc_f32_to_bf16(g * orc_dsilu(av));"),
+    # bf16 add: the second operand read from the first
+    "add_operand": ("orc_f32_to_bf16(orc_bf16_to_f32(x[i]) + orc_bf16_to_f32(y[i]))",
+                    "orc_f32_to_bf16(orc_bf16_to_f32(x[i]) + orc_bf16_to_f32(x[i]))"),
 }
 
 
