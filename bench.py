@@ -44,6 +44,9 @@ def parse():
                    help="output rows per GEMM in the CPU oracle sample")
     p.add_argument("--no-next-rows", action="store_true",
                    help="skip the next_rows measurements (profiling runs of the step alone)")
+    p.add_argument("--ffn-block-only", action="store_true",
+                   help="only measure the SwiGLU FFN block (profiling runs of its kernels); "
+                        "prints its JSON object and exits")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="only run 3 plain device copies of this many bytes (the "
                         "calibration kernel for HBM byte counters) and exit")
@@ -152,6 +155,68 @@ def measure_e5m2_step(steps, flops_per_step: int, reps: int = 10):
             "ms_per_step": round(el * 1e3 / reps, 4)}
 
 
+def measure_ffn_block(steps, wl, stream, reps: int = 5, e5m2_grad: bool = False):
+    """The SwiGLU feed-forward block on the FFN workload's tensors (x and W1
+    of w1, W3 of w3, W2 and dY of w2): x quantized once for w1 and w3, the
+    SwiGLU producers with the amax of h, da, db fused in, nine GEMMs.  Wall
+    time per step bracketed by device synchronisation; HIP events on the
+    launch stream around every launch for the split and the SwiGLU entry
+    points' bandwidth."""
+    import torch
+    from float8_mixed_precision_amd import ops
+
+    names = [l.name for l in wl.linears]
+    if names != ["w1", "w3", "w2"]:
+        return None
+    w1, w3, w2 = steps[0], steps[1], steps[2]
+    blk = ops.SwiGLUFFNStep(w1.x, w1.w, w3.w, w2.w, w2.dy, w1.rowwise, e5m2_grad=e5m2_grad)
+    M, D, H = blk.M, blk.D, blk.H
+    for _ in range(2):
+        blk.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        blk.run()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / reps
+    rec = []
+    for _ in range(reps):
+        for kind, work, fn in blk.ops():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            rec.append((kind, work, fn, e0, e1))
+    torch.cuda.synchronize()
+    split = {}
+    for kind in ("gemm", "quantize", "swiglu"):
+        split[kind] = round(sum(a.elapsed_time(b) for k, _, _, a, b in rec if k == kind) / reps, 4)
+    sw = {}
+    per = [(w, a.elapsed_time(b)) for k, w, _, a, b in rec if k == "swiglu"]
+    for i, name in enumerate(("swiglu_fwd", "swiglu_bwd")):
+        v = per[i::2]
+        work, ms = v[0][0], sum(t for _, t in v) / len(v)
+        ach = work / (ms * 1e-3) / 1e9
+        sw[name] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                    "bytes_per_call": work, "avg_call_us": round(ms * 1e3, 2)}
+    flops = blk.flops
+    # bytes of quantize traffic (amax pass + cast) per step, this block
+    # against the same block with x quantized per linear and plain
+    # quantizes of h, da, db after a SwiGLU that only writes them
+    fused = 6 * M * D * 2 + 18 * H * D + 4 * M * H + 8 * M * H
+    unfused = 6 * M * D * 3 + 18 * H * D + 6 * M * H + 12 * M * H
+    del blk
+    return {"metric": "SwiGLU FFN block fwd+bwd (shared quantize of x, amax fused into the "
+                      "SwiGLU producers)%s" % (", gradients E5M2" if e5m2_grad else ""),
+            "value": round(flops / wall / 1e12, 2), "unit": "TFLOP/s",
+            "shape": {"M": M, "D": D, "H": H}, "flops_per_step": flops, "steps": reps,
+            "ms_per_step": round(wall * 1e3, 4), "split_ms_per_step": split, **sw,
+            "quantize_bytes_per_step": {"block": fused, "unfused_block": unfused,
+                                        "saved_frac": round(1 - fused / unfused, 4)}}
+
+
 def measure_next_rows(steps, stream, reps: int = 5):
     """The entry points beyond the linear's own step, timed on the same FFN
     tensors after the main measurement (outside `value`): the shard amax and
@@ -239,6 +304,10 @@ def main():
                                     W.bits_to_torch(d["dy"], dev), wl.rowwise))
     del data
     stream = torch.cuda.current_stream()
+    if args.ffn_block_only:
+        print("[bench] ffn block only", file=sys.stderr, flush=True)
+        print(json.dumps(measure_ffn_block(steps, wl, stream, reps=args.steps)), flush=True)
+        return
 
     # per-op events: (kind, flops or bytes, start, end)
     def run_step(record):
@@ -338,6 +407,12 @@ def main():
         print("[bench] next rows", file=sys.stderr, flush=True)
         result["next_rows"] = measure_next_rows(steps, stream)
         result["next_rows"]["e5m2_grad_step"] = measure_e5m2_step(steps, wl.flops)
+        print("[bench] ffn block", file=sys.stderr, flush=True)
+        blk = measure_ffn_block(steps, wl, stream)
+        if blk is not None:
+            result["next_rows"]["ffn_block"] = blk
+            result["next_rows"]["ffn_block_e5m2"] = measure_ffn_block(steps, wl, stream,
+                                                                      e5m2_grad=True)
     del steps, shared
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libfp8linear.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "swiglu.hip"]
 ARCH = os.environ.get("FP8L_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

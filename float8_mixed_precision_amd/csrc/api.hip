@@ -164,6 +164,80 @@ int fp8_linear_bwd_w_f32(const void *dytq, const float *sdyt, const void *xtq,
   return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
 }
 
+int fp8_linear_bwd_x_acc(const void *dyq, const float *sdy, const void *wtq, const float *swt,
+                         int64_t M, int64_t N, int64_t K, int scaling, void *grad_x,
+                         void *stream) {
+  if (bad_scaling(scaling)) return FP8L_EINVAL;
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8L_ESHAPE;
+  if (bad_gemm_sizes(M, K, N)) return FP8L_ESHAPE;
+  int s = check_gemm_operands(dyq, sdy, wtq, swt, grad_x, M, K, N);
+  if (s != FP8L_OK) return s;
+  hipError_t e = fp8l::gemm_acc_launch(static_cast<const uint8_t *>(dyq), sdy,
+                                       static_cast<const uint8_t *>(wtq), swt,
+                                       (scaling & FP8L_ROWWISE) != 0,
+                                       (scaling & FP8L_E5M2) != 0, M, K, N,
+                                       static_cast<uint16_t *>(grad_x),
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
+size_t fp8_swiglu_workspace_bytes(int64_t rows, int64_t hidden, int scaling) {
+  if (bad_dim(rows) || bad_dim(hidden) || bad_scaling(scaling)) return 0;
+  return fp8l::swiglu_workspace_bytes(rows, hidden, scaling);
+}
+
+int fp8_swiglu_fwd(const void *a, const void *b, int64_t rows, int64_t hidden, int scaling,
+                   void *h, void *hq, void *hqt, float *scale, float *scale_t, float *amax_out,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  if (scaling != FP8L_TENSORWISE && scaling != FP8L_ROWWISE) return FP8L_EINVAL;
+  if (bad_dim(rows) || bad_dim(hidden) || rows * hidden > kMaxElems) return FP8L_ESHAPE;
+  const bool rw = scaling == FP8L_ROWWISE;
+  if ((!scale && (!rw || rows > 0)) || (!scale_t && (!rw || hidden > 0))) return FP8L_EINVAL;
+  if (rows * hidden > 0 && (!a || !b || !h || !hq || !hqt)) return FP8L_EINVAL;
+  const size_t need = fp8l::swiglu_workspace_bytes(rows, hidden, scaling);
+  if (!workspace) return FP8L_EINVAL;
+  if (workspace_bytes < need) return FP8L_EWORKSPACE;
+  if (misaligned(a) || misaligned(b) || misaligned(h) || misaligned(hq) || misaligned(hqt) ||
+      misaligned(workspace))
+    return FP8L_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(scale) & 3u) || (reinterpret_cast<uintptr_t>(scale_t) & 3u) ||
+      (reinterpret_cast<uintptr_t>(amax_out) & 3u))
+    return FP8L_EALIGN;
+  hipError_t e = fp8l::swiglu_fwd_launch(a, b, rows, hidden, scaling, h, hq, hqt, scale,
+                                         scale_t, amax_out, workspace,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
+int fp8_swiglu_bwd(const void *dh, const void *a, const void *b, int64_t rows, int64_t hidden,
+                   int scaling, void *da, void *db, void *daq, void *daqt, float *da_scale,
+                   float *da_scale_t, float *da_amax, void *dbq, void *dbqt, float *db_scale,
+                   float *db_scale_t, float *db_amax, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+  if (bad_scaling(scaling)) return FP8L_EINVAL;
+  if (bad_dim(rows) || bad_dim(hidden) || rows * hidden > kMaxElems) return FP8L_ESHAPE;
+  const bool rw = (scaling & FP8L_ROWWISE) != 0;
+  if ((!da_scale || !db_scale) && (!rw || rows > 0)) return FP8L_EINVAL;
+  if ((!da_scale_t || !db_scale_t) && (!rw || hidden > 0)) return FP8L_EINVAL;
+  if (rows * hidden > 0 &&
+      (!dh || !a || !b || !da || !db || !daq || !daqt || !dbq || !dbqt))
+    return FP8L_EINVAL;
+  const size_t need = fp8l::swiglu_workspace_bytes(rows, hidden, scaling);
+  if (!workspace) return FP8L_EINVAL;
+  if (workspace_bytes < need) return FP8L_EWORKSPACE;
+  if (misaligned(dh) || misaligned(a) || misaligned(b) || misaligned(da) || misaligned(db) ||
+      misaligned(daq) || misaligned(daqt) || misaligned(dbq) || misaligned(dbqt) ||
+      misaligned(workspace))
+    return FP8L_EALIGN;
+  for (const float *f : {da_scale, da_scale_t, da_amax, db_scale, db_scale_t, db_amax})
+    if (reinterpret_cast<uintptr_t>(f) & 3u) return FP8L_EALIGN;
+  const fp8l::Fp8Out qa = {daq, daqt, da_scale, da_scale_t, da_amax};
+  const fp8l::Fp8Out qb = {dbq, dbqt, db_scale, db_scale_t, db_amax};
+  hipError_t e = fp8l::swiglu_bwd_launch(dh, a, b, rows, hidden, scaling, da, db, qa, qb,
+                                         workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
 int fp8_linear_encode_e4m3(const float *in, uint8_t *out, int64_t n, void *stream) {
   if (n < 0 || n > kMaxElems) return FP8L_ESHAPE;
   if (n == 0) return FP8L_OK;

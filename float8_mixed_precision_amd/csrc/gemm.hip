@@ -149,12 +149,15 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m,
 // (the scaled value before bf16 rounding) instead of bf16.  FA: code format
 // of A (0 = E4M3, 1 = E5M2 gradients); B is E4M3.  The instruction's
 // format selectors apply to its first and second source operand, here the
-// B and the A fragment.
-template <bool KFULL, bool RW, bool F32, int FA>
+// B and the A fragment.  ACC (bf16 output only): C holds a bf16 matrix on
+// entry and receives bf16(fl32(C) + fl32(bf16 result)), the sum of two
+// gradient contributions as bf16 tensors add.
+template <bool KFULL, bool RW, bool F32, int FA, bool ACC>
 __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
     const uint8_t *__restrict__ A, const float *__restrict__ sa,
     const uint8_t *__restrict__ B, const float *__restrict__ sb,
     int M, int N, int K, void *__restrict__ C, int tiles_m, int tiles_n) {
+  static_assert(!(F32 && ACC), "accumulation is into a bf16 output");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[INV_OFF + (RW ? INV_BYTES : 0)];
 
   const int tid = threadIdx.x;
@@ -493,12 +496,31 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
       const int id = (it0 + u) * 64 + lane_e;
       v[u] = *reinterpret_cast<const v4u *>(ep + (id >> 4) * EP_STRIDE + (id & 15) * 16);
     }
+    uint32_t off[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const bool ok = col_ok && (it0 + u) * 4 < rows_left;
-      const uint32_t off = ok ? soff0 + (uint32_t)(it0 + u) * row_step : OOB_C;
-      __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off, 0, 0);
+      off[u] = ok ? soff0 + (uint32_t)(it0 + u) * row_step : OOB_C;
     }
+    if (ACC) {
+      // the bf16 values already in C (offsets outside read as 0), added in
+      // fp32 and rounded once to bf16 (round to nearest even)
+      v4u cin[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cin[u] = __builtin_amdgcn_raw_buffer_load_b128(rsC, off[u], 0, 0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t x = v[u][d], y = cin[u][d];
+          const f32x2 sum = {__uint_as_float(x << 16) + __uint_as_float(y << 16),
+                             __uint_as_float(x & 0xFFFF0000u) + __uint_as_float(y & 0xFFFF0000u)};
+          v[u][d] = __builtin_bit_cast(uint32_t, __builtin_convertvector(sum, bf16x2));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off[u], 0, 0);
   }
 }
 
@@ -506,7 +528,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
 
 namespace {
 
-template <bool F32, int FA>
+template <bool F32, int FA, bool ACC = false>
 hipError_t launch_variant(const uint8_t *A, const float *sa, const uint8_t *B,
                           const float *sb, int rowwise, int64_t M, int64_t N, int64_t K,
                           void *C, hipStream_t stream) {
@@ -515,10 +537,10 @@ hipError_t launch_variant(const uint8_t *A, const float *sa, const uint8_t *B,
   const int tiles_n = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   const bool kfull = K % BK == 0;
-  auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true, F32, FA>
-                               : k_gemm_fp8_tn<false, true, F32, FA>)
-                      : (kfull ? k_gemm_fp8_tn<true, false, F32, FA>
-                               : k_gemm_fp8_tn<false, false, F32, FA>);
+  auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true, F32, FA, ACC>
+                               : k_gemm_fp8_tn<false, true, F32, FA, ACC>)
+                      : (kfull ? k_gemm_fp8_tn<true, false, F32, FA, ACC>
+                               : k_gemm_fp8_tn<false, false, F32, FA, ACC>);
   hipLaunchKernelGGL(kern, grid, dim3(THREADS), 0, stream, A, sa, B, sb, (int)M, (int)N,
                      (int)K, C, tiles_m, tiles_n);
   return hipGetLastError();
@@ -531,6 +553,13 @@ hipError_t gemm_launch(const uint8_t *A, const float *sa, const uint8_t *B,
                        int64_t K, uint16_t *C, hipStream_t stream) {
   return fmt_a ? launch_variant<false, 1>(A, sa, B, sb, rowwise, M, N, K, C, stream)
                : launch_variant<false, 0>(A, sa, B, sb, rowwise, M, N, K, C, stream);
+}
+
+hipError_t gemm_acc_launch(const uint8_t *A, const float *sa, const uint8_t *B,
+                           const float *sb, int rowwise, int fmt_a, int64_t M, int64_t N,
+                           int64_t K, uint16_t *C, hipStream_t stream) {
+  return fmt_a ? launch_variant<false, 1, true>(A, sa, B, sb, rowwise, M, N, K, C, stream)
+               : launch_variant<false, 0, true>(A, sa, B, sb, rowwise, M, N, K, C, stream);
 }
 
 hipError_t gemm_f32_launch(const uint8_t *A, const float *sa, const uint8_t *B,

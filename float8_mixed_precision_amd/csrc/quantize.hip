@@ -25,56 +25,17 @@
 namespace fp8l {
 namespace {
 
-// rowwise amax tile: 64 rows x 256 columns per 256-thread workgroup.  Each
-// thread owns one 8-column chunk (16 bytes of bf16) and walks 8 of the
-// tile's rows.
-constexpr int AM_TR = 64;
-constexpr int AM_TC = 256;
-constexpr int AM_THREADS = 256;
-
 // tensorwise amax: chunks of 256 threads x 8 loads of 16 bytes (32 KB),
 // at most TW_MAX_BLOCKS workgroups in a grid-stride loop.  Workspace: one
-// u32 partial maximum per block.
+// u32 partial maximum per block.  (The rowwise tile AM_TR x AM_TC and
+// TW_MAX_BLOCKS are in fp8l_internal.h: producer kernels elsewhere write
+// partials in the same layouts.)
 constexpr int TW_UNROLL = 8;
 constexpr int TW_CHUNK = AM_THREADS * TW_UNROLL;   // 16-byte vectors per chunk
-constexpr int TW_MAX_BLOCKS = 512;
 
 // cast tile: 128 rows x 128 columns per 256-thread workgroup.
 constexpr int CT_T = 128;
 constexpr int CT_THREADS = 256;
-
-__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
-  uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
-  uint32_t hi = max(a >> 16, b >> 16);
-  return lo | (hi << 16);
-}
-
-// max over the two u16 halves of a dword
-__device__ __forceinline__ uint32_t hmax16(uint32_t a) {
-  return max(a & 0xFFFFu, a >> 16);
-}
-
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
-
-// max over the 32 lanes of each half-wave
-__device__ __forceinline__ uint32_t half_wave_max(uint32_t v) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
-
-struct U4 {
-  uint32_t x, y, z, w;
-};
-
-__device__ __forceinline__ U4 load16(const void *p) {
-  uint4 v = *reinterpret_cast<const uint4 *>(p);
-  return {v.x, v.y, v.z, v.w};
-}
 
 // ----------------------------------------------------------------- amax --
 //
@@ -418,34 +379,22 @@ size_t quantize_workspace_bytes(int64_t rows, int64_t cols, int scaling) {
 namespace {
 
 template <int FMT>
-hipError_t quantize_launch_fmt(const void *x, int64_t rows, int64_t cols, bool rowwise,
-                               void *q, void *qt, float *scale, float *scale_t,
-                               float *amax_out, void *workspace, hipStream_t stream) {
-  const AmaxGeom g = amax_geom(rows, cols);
-  const int64_t ntiles = g.tiles_r * g.tiles_c;
+hipError_t finish_fmt(const void *x, int64_t rows, int64_t cols, bool rowwise, int nparts,
+                      void *q, void *qt, float *scale, float *scale_t, float *amax_out,
+                      void *workspace, hipStream_t stream) {
   const uint16_t *xb = static_cast<const uint16_t *>(x);
   const int R = (int)rows, C = (int)cols;
-  const int64_t nb = rowwise ? 0 : tw_blocks(rows, cols);
-  uint32_t *part = static_cast<uint32_t *>(workspace);
-  if (!rowwise) {
-    if (nb > 0)
-      hipLaunchKernelGGL(k_amax_tw, dim3((unsigned)nb), dim3(AM_THREADS), 0, stream,
-                         static_cast<const uint4 *>(x), rows * cols / 8, part);
-    else
-      hipLaunchKernelGGL(k_finalize_tw_empty<FMT>, dim3(1), dim3(64), 0, stream, scale,
-                         scale_t, amax_out);
-  } else {
-    uint16_t *rowpart = static_cast<uint16_t *>(workspace);
-    // column partials start on a 256-byte boundary after the row partials
-    size_t off = ((size_t)(g.tiles_c * rows) * sizeof(uint16_t) + 255) & ~(size_t)255;
-    uint16_t *colpart = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(workspace) + off);
-    if (ntiles > 0)
-      hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)ntiles), dim3(AM_THREADS), 0,
-                         stream, xb, R, C, (int)g.tiles_c, rowpart, colpart);
+  if (rowwise) {
+    const AmaxGeom g = amax_geom(rows, cols);
+    uint16_t *rowpart, *colpart;
+    quantize_rowwise_partials(workspace, rows, cols, &rowpart, &colpart);
     if (rows + cols > 0)
       hipLaunchKernelGGL(k_finalize_rowwise<FMT>, dim3((unsigned)cdiv(rows + cols, 256)),
                          dim3(256), 0, stream, rowpart, colpart, R, C, (int)g.tiles_c,
                          (int)g.tiles_r, scale, scale_t, amax_out);
+  } else if (nparts == 0) {
+    hipLaunchKernelGGL(k_finalize_tw_empty<FMT>, dim3(1), dim3(64), 0, stream, scale,
+                       scale_t, amax_out);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -454,8 +403,8 @@ hipError_t quantize_launch_fmt(const void *x, int64_t rows, int64_t cols, bool r
     if (!rowwise)
       hipLaunchKernelGGL((k_cast_transpose<MODE_TW, FMT>), dim3((unsigned)(ct_r * ct_c)),
                          dim3(CT_THREADS), 0, stream, xb, R, C, (int)ct_c, scale, scale_t,
-                         part, (int)nb, amax_out, static_cast<uint8_t *>(q),
-                         static_cast<uint8_t *>(qt));
+                         static_cast<const uint32_t *>(workspace), nparts, amax_out,
+                         static_cast<uint8_t *>(q), static_cast<uint8_t *>(qt));
     else
       hipLaunchKernelGGL((k_cast_transpose<MODE_RW, FMT>), dim3((unsigned)(ct_r * ct_c)),
                          dim3(CT_THREADS), 0, stream, xb, R, C, (int)ct_c, scale, scale_t,
@@ -465,7 +414,54 @@ hipError_t quantize_launch_fmt(const void *x, int64_t rows, int64_t cols, bool r
   return hipGetLastError();
 }
 
+// first pass (amax partial maxima of x), then the second half
+template <int FMT>
+hipError_t quantize_launch_fmt(const void *x, int64_t rows, int64_t cols, bool rowwise,
+                               void *q, void *qt, float *scale, float *scale_t,
+                               float *amax_out, void *workspace, hipStream_t stream) {
+  const AmaxGeom g = amax_geom(rows, cols);
+  const int64_t ntiles = g.tiles_r * g.tiles_c;
+  const int64_t nb = rowwise ? 0 : tw_blocks(rows, cols);
+  if (!rowwise) {
+    if (nb > 0)
+      hipLaunchKernelGGL(k_amax_tw, dim3((unsigned)nb), dim3(AM_THREADS), 0, stream,
+                         static_cast<const uint4 *>(x), rows * cols / 8,
+                         static_cast<uint32_t *>(workspace));
+  } else if (ntiles > 0) {
+    uint16_t *rowpart, *colpart;
+    quantize_rowwise_partials(workspace, rows, cols, &rowpart, &colpart);
+    hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)ntiles), dim3(AM_THREADS), 0, stream,
+                       static_cast<const uint16_t *>(x), (int)rows, (int)cols,
+                       (int)g.tiles_c, rowpart, colpart);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return finish_fmt<FMT>(x, rows, cols, rowwise, (int)nb, q, qt, scale, scale_t, amax_out,
+                         workspace, stream);
+}
+
 }  // namespace
+
+void quantize_rowwise_partials(void *workspace, int64_t rows, int64_t cols,
+                               uint16_t **rowpart, uint16_t **colpart) {
+  const AmaxGeom g = amax_geom(rows, cols);
+  // column partials start on a 256-byte boundary after the row partials
+  const size_t off = ((size_t)(g.tiles_c * rows) * sizeof(uint16_t) + 255) & ~(size_t)255;
+  *rowpart = static_cast<uint16_t *>(workspace);
+  *colpart = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(workspace) + off);
+}
+
+hipError_t quantize_finish_launch(const void *x, int64_t rows, int64_t cols, int scaling,
+                                  int nparts, void *q, void *qt, float *scale,
+                                  float *scale_t, float *amax_out, void *workspace,
+                                  hipStream_t stream) {
+  const bool rw = (scaling & FP8L_ROWWISE) != 0;
+  if (scaling & FP8L_E5M2)
+    return finish_fmt<1>(x, rows, cols, rw, nparts, q, qt, scale, scale_t, amax_out,
+                         workspace, stream);
+  return finish_fmt<0>(x, rows, cols, rw, nparts, q, qt, scale, scale_t, amax_out, workspace,
+                       stream);
+}
 
 hipError_t quantize_launch(const void *x, int64_t rows, int64_t cols,
                            int scaling, void *q, void *qt, float *scale,

@@ -24,8 +24,9 @@ FP8L_OK, FP8L_EINVAL, FP8L_ESHAPE, FP8L_EALIGN, FP8L_EWORKSPACE, FP8L_EHIP = ran
 FP8L_TENSORWISE, FP8L_ROWWISE, FP8L_E5M2 = 0, 1, 2
 EXPORTS = ("fp8_linear_workspace_bytes", "fp8_linear_quantize", "fp8_linear_amax",
            "fp8_linear_quantize_scaled", "fp8_linear_fwd", "fp8_linear_bwd",
-           "fp8_linear_bwd_w_f32", "fp8_linear_encode_e4m3", "fp8_linear_encode_e5m2",
-           "fp8_linear_status_string", "fp8_linear_version")
+           "fp8_linear_bwd_w_f32", "fp8_linear_bwd_x_acc", "fp8_linear_encode_e4m3",
+           "fp8_linear_encode_e5m2", "fp8_swiglu_workspace_bytes", "fp8_swiglu_fwd",
+           "fp8_swiglu_bwd", "fp8_linear_status_string", "fp8_linear_version")
 
 
 class Fp8LinearError(RuntimeError):
@@ -61,6 +62,15 @@ def lib() -> ctypes.CDLL:
     L.fp8_linear_quantize_scaled.argtypes = [P, i64, i64, P, P, P, P]
     L.fp8_linear_bwd_w_f32.restype = I
     L.fp8_linear_bwd_w_f32.argtypes = [P, P, P, P, i64, i64, i64, I, P, P]
+    L.fp8_linear_bwd_x_acc.restype = I
+    L.fp8_linear_bwd_x_acc.argtypes = [P, P, P, P, i64, i64, i64, I, P, P]
+    L.fp8_swiglu_workspace_bytes.restype = ctypes.c_size_t
+    L.fp8_swiglu_workspace_bytes.argtypes = [i64, i64, I]
+    L.fp8_swiglu_fwd.restype = I
+    L.fp8_swiglu_fwd.argtypes = [P, P, i64, i64, I, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.fp8_swiglu_bwd.restype = I
+    L.fp8_swiglu_bwd.argtypes = ([P, P, P, i64, i64, I, P, P] + [P] * 10
+                                 + [P, ctypes.c_size_t, P])
     L.fp8_linear_encode_e4m3.restype = I
     L.fp8_linear_encode_e4m3.argtypes = [P, P, i64, P]
     L.fp8_linear_encode_e5m2.restype = I
@@ -221,6 +231,73 @@ def fp8_linear_bwd_w_f32(dytq, sdyt, xtq, sxt, M: int, N: int, K: int,
     return grad_w
 
 
+def fp8_linear_bwd_x_acc(dyq, sdy, wtq, swt, M: int, N: int, K: int, grad_x: torch.Tensor,
+                         rowwise: bool = False, stream=None, e5m2: bool = False) -> torch.Tensor:
+    """grad_x [M, K] (bf16, in place) = bf16(grad_x + bf16(dY . W)): the second
+    gradient contribution of an x that feeds two linears."""
+    _check(lib().fp8_linear_bwd_x_acc(_p(dyq), _p(sdy), _p(wtq), _p(swt), M, N, K,
+                                      _scaling(rowwise, e5m2), _p(grad_x), _stream(stream)),
+           "fp8_linear_bwd_x_acc")
+    return grad_x
+
+
+def fp8_swiglu_workspace_bytes(rows: int, hidden: int, rowwise: bool = False,
+                               e5m2: bool = False) -> int:
+    return int(lib().fp8_swiglu_workspace_bytes(rows, hidden, _scaling(rowwise, e5m2)))
+
+
+def alloc_swiglu_workspace(rows: int, hidden: int, rowwise: bool, device) -> torch.Tensor:
+    return torch.zeros(max(fp8_swiglu_workspace_bytes(rows, hidden, rowwise), 256),
+                       dtype=torch.uint8, device=device)
+
+
+def fp8_swiglu_fwd(a: torch.Tensor, b: torch.Tensor, rowwise: bool = False,
+                   h: Optional[torch.Tensor] = None, out: Optional[Quantized] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> Tuple[torch.Tensor, Quantized]:
+    """h = silu(a) * b (bf16 [rows, hidden]) and the E4M3 quantize of h."""
+    assert a.dtype == b.dtype == torch.bfloat16 and a.shape == b.shape and a.dim() == 2
+    assert a.is_contiguous() and b.is_contiguous()
+    rows, hidden = a.shape
+    if h is None:
+        h = torch.empty_like(a)
+    if out is None:
+        out = alloc_quantized(rows, hidden, rowwise, a.device)
+    if workspace is None:
+        workspace = alloc_swiglu_workspace(rows, hidden, rowwise, a.device)
+    _check(lib().fp8_swiglu_fwd(_p(a), _p(b), rows, hidden, _scaling(rowwise), _p(h),
+                                _p(out.q), _p(out.qt), _p(out.scale), _p(out.scale_t),
+                                _p(out.amax), _p(workspace), workspace.numel(),
+                                _stream(stream)), "fp8_swiglu_fwd")
+    return h, out
+
+
+def fp8_swiglu_bwd(dh: torch.Tensor, a: torch.Tensor, b: torch.Tensor, rowwise: bool = False,
+                   da: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None,
+                   qa: Optional[Quantized] = None, qb: Optional[Quantized] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None,
+                   e5m2: bool = False):
+    """(da, db, quantize of da, quantize of db) for h = silu(a) * b and the
+    gradient dh; codes E5M2 when e5m2."""
+    assert dh.shape == a.shape == b.shape and a.dim() == 2
+    assert dh.dtype == a.dtype == b.dtype == torch.bfloat16
+    assert dh.is_contiguous() and a.is_contiguous() and b.is_contiguous()
+    rows, hidden = a.shape
+    dev = a.device
+    da = torch.empty_like(a) if da is None else da
+    db = torch.empty_like(a) if db is None else db
+    qa = alloc_quantized(rows, hidden, rowwise, dev) if qa is None else qa
+    qb = alloc_quantized(rows, hidden, rowwise, dev) if qb is None else qb
+    if workspace is None:
+        workspace = alloc_swiglu_workspace(rows, hidden, rowwise, dev)
+    _check(lib().fp8_swiglu_bwd(_p(dh), _p(a), _p(b), rows, hidden, _scaling(rowwise, e5m2),
+                                _p(da), _p(db), _p(qa.q), _p(qa.qt), _p(qa.scale),
+                                _p(qa.scale_t), _p(qa.amax), _p(qb.q), _p(qb.qt), _p(qb.scale),
+                                _p(qb.scale_t), _p(qb.amax), _p(workspace), workspace.numel(),
+                                _stream(stream)), "fp8_swiglu_bwd")
+    return da, db, qa, qb
+
+
 def fp8_linear_encode_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None,
                            stream=None) -> torch.Tensor:
     """Device E4M3 saturating RNE codes of fp32 values."""
@@ -293,3 +370,120 @@ class LinearStep:
     def run(self, stream=None):
         self.quantize(stream)
         self.gemms(stream)
+
+
+# ------------------------------------------------------ SwiGLU FFN block --
+
+class SwiGLUFFNStep:
+    """One Float8 SwiGLU feed-forward block fwd+bwd on preallocated buffers.
+
+    x [M, D], w1 and w3 [H, D], w2 [D, H], d_out [M, D] (bf16).  ``run()``
+    enqueues, on the current stream:
+
+      quantize x once (read by w1 and w3), quantize w1, w3, w2
+      a = x.w1^T, b = x.w3^T                       (fp8 GEMMs)
+      h = silu(a) * b and its quantize             (fp8_swiglu_fwd)
+      out = h.w2^T
+      quantize d_out
+      dh = d_out.w2, grad_w2 = d_out^T.h
+      da, db and their quantizes                   (fp8_swiglu_bwd)
+      grad_x = da.w1, then += db.w3                (fp8_linear_bwd_x_acc)
+      grad_w1 = da^T.x, grad_w3 = db^T.x
+
+    With ``e5m2_grad`` the gradient operands (d_out, da, db) are E5M2.
+    """
+
+    def __init__(self, x, w1, w3, w2, d_out, rowwise: bool = False, e5m2_grad: bool = False):
+        self.x, self.w1, self.w3, self.w2, self.d_out = x, w1, w3, w2, d_out
+        self.rowwise, self.e5m2_grad = rowwise, e5m2_grad
+        self.M, self.D = x.shape
+        self.H = w1.shape[0]
+        assert w1.shape == w3.shape == (self.H, self.D) and w2.shape == (self.D, self.H)
+        assert d_out.shape == (self.M, self.D)
+        M, D, H, dev = self.M, self.D, self.H, x.device
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        self.qx = alloc_quantized(M, D, rowwise, dev)
+        self.qw1 = alloc_quantized(H, D, rowwise, dev)
+        self.qw3 = alloc_quantized(H, D, rowwise, dev)
+        self.qw2 = alloc_quantized(D, H, rowwise, dev)
+        self.qh = alloc_quantized(M, H, rowwise, dev)
+        self.qdy = alloc_quantized(M, D, rowwise, dev)
+        self.qda = alloc_quantized(M, H, rowwise, dev)
+        self.qdb = alloc_quantized(M, H, rowwise, dev)
+        ws = max(fp8_linear_workspace_bytes(r, c, rowwise) for r, c in
+                 ((M, D), (H, D), (D, H)))
+        self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.ws_sw = alloc_swiglu_workspace(M, H, rowwise, dev)
+        self.a = torch.empty((M, H), **bf)
+        self.b = torch.empty((M, H), **bf)
+        self.h = torch.empty((M, H), **bf)
+        self.out = torch.empty((M, D), **bf)
+        self.dh = torch.empty((M, H), **bf)
+        self.da = torch.empty((M, H), **bf)
+        self.db = torch.empty((M, H), **bf)
+        self.grad_x = torch.empty((M, D), **bf)
+        self.grad_w1 = torch.empty((H, D), **bf)
+        self.grad_w3 = torch.empty((H, D), **bf)
+        self.grad_w2 = torch.empty((D, H), **bf)
+
+    @property
+    def flops(self) -> int:
+        """Nine GEMMs of 2*M*D*H each."""
+        return 18 * self.M * self.D * self.H
+
+    def ops(self):
+        """The launches of one step, in order: (kind, work, fn) with kind one
+        of "quantize", "swiglu", "gemm" and work the algorithmic bytes
+        (quantize / swiglu) or flops (gemm) of the launch."""
+        M, D, H, rw, e5 = self.M, self.D, self.H, self.rowwise, self.e5m2_grad
+        g = 2 * M * D * H
+        return (
+            ("quantize", 6 * M * D, lambda: fp8_linear_quantize(self.x, rw, self.qx, self.ws)),
+            ("quantize", 6 * H * D, lambda: fp8_linear_quantize(self.w1, rw, self.qw1, self.ws)),
+            ("quantize", 6 * H * D, lambda: fp8_linear_quantize(self.w3, rw, self.qw3, self.ws)),
+            ("quantize", 6 * D * H, lambda: fp8_linear_quantize(self.w2, rw, self.qw2, self.ws)),
+            ("gemm", g, lambda: fp8_linear_fwd(self.qx.q, self.qx.scale, self.qw1.q,
+                                               self.qw1.scale, rw, self.a)),
+            ("gemm", g, lambda: fp8_linear_fwd(self.qx.q, self.qx.scale, self.qw3.q,
+                                               self.qw3.scale, rw, self.b)),
+            # a, b read twice (elementwise pass, then h read by the cast),
+            # h written once; q and qt written
+            ("swiglu", 10 * M * H, lambda: fp8_swiglu_fwd(self.a, self.b, rw, self.h, self.qh,
+                                                          self.ws_sw)),
+            ("gemm", g, lambda: fp8_linear_fwd(self.qh.q, self.qh.scale, self.qw2.q,
+                                               self.qw2.scale, rw, self.out)),
+            ("quantize", 6 * M * D, lambda: fp8_linear_quantize(self.d_out, rw, self.qdy,
+                                                                self.ws, e5m2=e5)),
+            ("gemm", g, lambda: fp8_linear_bwd(self.qdy.q, self.qdy.scale, None, None,
+                                               self.qw2.qt, self.qw2.scale_t, None, None,
+                                               M, D, H, rw, grad_x=self.dh, want_w=False,
+                                               e5m2=e5)),
+            ("gemm", g, lambda: fp8_linear_bwd(None, None, self.qdy.qt, self.qdy.scale_t,
+                                               None, None, self.qh.qt, self.qh.scale_t,
+                                               M, D, H, rw, grad_w=self.grad_w2, want_x=False,
+                                               e5m2=e5)),
+            # dh, a, b read; da, db written; each read again by its cast,
+            # whose q and qt are written
+            ("swiglu", 18 * M * H, lambda: fp8_swiglu_bwd(self.dh, self.a, self.b, rw, self.da,
+                                                          self.db, self.qda, self.qdb,
+                                                          self.ws_sw, e5m2=e5)),
+            ("gemm", g, lambda: fp8_linear_bwd(self.qda.q, self.qda.scale, None, None,
+                                               self.qw1.qt, self.qw1.scale_t, None, None,
+                                               M, H, D, rw, grad_x=self.grad_x, want_w=False,
+                                               e5m2=e5)),
+            ("gemm", g, lambda: fp8_linear_bwd_x_acc(self.qdb.q, self.qdb.scale, self.qw3.qt,
+                                                     self.qw3.scale_t, M, H, D, self.grad_x,
+                                                     rw, e5m2=e5)),
+            ("gemm", g, lambda: fp8_linear_bwd(None, None, self.qda.qt, self.qda.scale_t,
+                                               None, None, self.qx.qt, self.qx.scale_t,
+                                               M, H, D, rw, grad_w=self.grad_w1, want_x=False,
+                                               e5m2=e5)),
+            ("gemm", g, lambda: fp8_linear_bwd(None, None, self.qdb.qt, self.qdb.scale_t,
+                                               None, None, self.qx.qt, self.qx.scale_t,
+                                               M, H, D, rw, grad_w=self.grad_w3, want_x=False,
+                                               e5m2=e5)),
+        )
+
+    def run(self):
+        for _, _, fn in self.ops():
+            fn()

@@ -210,6 +210,83 @@ FP8L_API int fp8_linear_bwd_w_f32(const void *dytq, const float *sdyt, const voi
                                   int scaling, float *grad_w, void *stream);
 
 /*
+ * grad_X added into an existing bf16 grad_x: for an x that feeds two linears
+ * (w1 and w3 of the SwiGLU feed-forward below), whose gradient is the sum of
+ * the two contributions as bf16 tensors add (autograd accumulates the
+ * gradient of a tensor used twice):
+ *
+ *   grad_x[m][k] = bf16( fl32(grad_x[m][k]) + fl32(g[m][k]) ),
+ *   g[m][k]      = fp8_linear_bwd's grad_x for these operands (bf16)
+ *
+ * dyq, sdy, wtq, swt, M, N, K, scaling as for fp8_linear_bwd's grad_x;
+ * grad_x [M, K] bf16 (device, read and written).
+ */
+FP8L_API int fp8_linear_bwd_x_acc(const void *dyq, const float *sdy, const void *wtq,
+                                  const float *swt, int64_t M, int64_t N, int64_t K,
+                                  int scaling, void *grad_x, void *stream);
+
+/*
+ * SwiGLU feed-forward of the Llama 3.1 model the pages train (the
+ * "torchtitan" tutorial page, Part II, "Using it", llama3_8b; Part V splits
+ * its hidden dimension across tensor-parallel ranks):
+ *
+ *   a = x W1^T,  b = x W3^T   [rows, hidden]   (two Float8 linears; x is
+ *                                               quantized once for both)
+ *   h = silu(a) * b           [rows, hidden]   (fp8_swiglu_fwd)
+ *   out = h W2^T                               (Float8 linear on h)
+ *
+ * The SwiGLU elementwise is the producer of w2's input, and of the output
+ * gradients of w1 and w3 in the backward; these entry points write the
+ * bf16 result and take its amax partial maxima in the same pass, so its
+ * quantize needs only the cast pass afterwards (one read of the tensor
+ * fewer than fp8_linear_quantize on the bf16 result).
+ *
+ * Elementwise definitions (silu(a) = a / (1 + e^-a); sigma(a) = 1/(1+e^-a);
+ * silu'(a) = sigma(a) (1 + a (1 - sigma(a))); silu and silu' are the fp32
+ * roundings of their exact values -- computed in fp64 -- and each other
+ * operation is one fp32 operation):
+ *   h  = bf16( fl32( silu(a) * b ) )
+ *   da = bf16( fl32( fl32(dh * b) * silu'(a) ) )
+ *   db = bf16( fl32( dh * silu(a) ) )
+ * followed by fp8_linear_quantize's definition applied to h (E4M3), or to
+ * da and db separately (E4M3, or E5M2 with that flag), each with its own
+ * scales.
+ *
+ * Every matrix is a separate dense [rows, hidden] array; rows and hidden
+ * are multiples of 16.  The workspace (>= fp8_swiglu_workspace_bytes) holds
+ * the partial maxima; contents undefined on entry and exit, not shared by
+ * calls in flight together.  An empty matrix writes only the scales of the
+ * empty set.
+ */
+FP8L_API size_t fp8_swiglu_workspace_bytes(int64_t rows, int64_t hidden, int scaling);
+
+/*
+ *   a, b      [rows, hidden] bf16 (device, read only)
+ *   h         [rows, hidden] bf16 (device, written)
+ *   hq, hqt, scale, scale_t, amax_out: as fp8_linear_quantize's q, qt, scale,
+ *             scale_t, amax_out for x = h (scaling: FP8L_TENSORWISE or
+ *             FP8L_ROWWISE; codes E4M3)
+ */
+FP8L_API int fp8_swiglu_fwd(const void *a, const void *b, int64_t rows, int64_t hidden,
+                            int scaling, void *h, void *hq, void *hqt, float *scale,
+                            float *scale_t, float *amax_out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ *   dh, a, b  [rows, hidden] bf16 (device, read only): dh is the gradient of h
+ *   da, db    [rows, hidden] bf16 (device, written)
+ *   daq, daqt, da_scale, da_scale_t, da_amax: the quantize of da, as
+ *             fp8_linear_quantize's outputs for x = da; likewise db*
+ *   scaling   FP8L_TENSORWISE or FP8L_ROWWISE, optionally | FP8L_E5M2
+ */
+FP8L_API int fp8_swiglu_bwd(const void *dh, const void *a, const void *b, int64_t rows,
+                            int64_t hidden, int scaling, void *da, void *db, void *daq,
+                            void *daqt, float *da_scale, float *da_scale_t, float *da_amax,
+                            void *dbq, void *dbqt, float *db_scale, float *db_scale_t,
+                            float *db_amax, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
  * The element conversion the quantize kernels use, exposed for testing it on
  * every fp32 input: out[i] = e4m3_sat_rne(in[i]) (definition above; a NaN
  * input gives a NaN code).  in: n fp32, out: n bytes, both device pointers.

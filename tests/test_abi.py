@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "fp8_linear.h")
 
 def declared_symbols():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"FP8L_API\s+[\w\s\*]*?\b(fp8_linear_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"FP8L_API\s+[\w\s\*]*?\b(fp8_\w+)\s*\(", src)))
 
 
 def test_header_declares_the_boundary():
@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\bT\s+(fp8_linear_\w+)", out))
+    exported = set(re.findall(r"\bT\s+(fp8_\w+)", out))
     assert set(declared_symbols()) <= exported
     L = ops.lib()
     for s in declared_symbols():
@@ -187,3 +187,61 @@ def test_amax_scaled_and_f32_entry_points_reject_bad_arguments():
     assert bw(gw=None) == E.FP8L_EINVAL
     assert bw(sxt=None) == E.FP8L_EINVAL
     assert bw(gw=A_BAD) == E.FP8L_EALIGN
+
+
+@pytestmark_cpu
+def test_swiglu_and_accumulate_entry_points_reject_bad_arguments():
+    E = ops
+    L = ops.lib()
+    P = ctypes.c_void_p
+    assert L.fp8_swiglu_workspace_bytes(24, 16, 0) == 0
+    assert L.fp8_swiglu_workspace_bytes(16, 16, 4) == 0
+    assert 0 < L.fp8_swiglu_workspace_bytes(8192, 14336, 0) < \
+        L.fp8_swiglu_workspace_bytes(8192, 14336, 1)
+
+    def fwd(a=A16, b=A16, rows=16, hidden=16, scaling=0, h=A16, q=A16, qt=A16, s=A16,
+            st=A16, amax=None, ws=A16, wsb=1 << 20):
+        v = lambda x: P(x) if x else None
+        return L.fp8_swiglu_fwd(v(a), v(b), rows, hidden, scaling, v(h), v(q), v(qt), v(s),
+                                v(st), v(amax), v(ws), wsb, None)
+
+    assert fwd(scaling=E.FP8L_E5M2) == E.FP8L_EINVAL      # h is an activation: E4M3 only
+    assert fwd(scaling=4) == E.FP8L_EINVAL
+    assert fwd(hidden=40) == E.FP8L_ESHAPE
+    assert fwd(rows=-16) == E.FP8L_ESHAPE
+    for k in ("a", "b", "h", "q", "qt", "s", "st", "ws"):
+        assert fwd(**{k: None}) == E.FP8L_EINVAL, k
+    assert fwd(wsb=16) == E.FP8L_EWORKSPACE
+    for k in ("a", "b", "h", "q", "qt", "ws"):
+        assert fwd(**{k: A_BAD}) == E.FP8L_EALIGN, k
+    assert fwd(s=A16 + 2) == E.FP8L_EALIGN
+
+    names = ("dh", "a", "b", "da", "db", "daq", "daqt", "das", "dast", "daam", "dbq", "dbqt",
+             "dbs", "dbst", "dbam", "ws")
+
+    def bwd(rows=16, hidden=16, scaling=0, wsb=1 << 20, **kw):
+        ptr = {n: kw.get(n, A16 if not n.endswith("am") else None) for n in names}
+        v = lambda x: P(x) if x else None
+        return L.fp8_swiglu_bwd(v(ptr["dh"]), v(ptr["a"]), v(ptr["b"]), rows, hidden, scaling,
+                                *[v(ptr[n]) for n in names[3:15]], v(ptr["ws"]), wsb, None)
+
+    assert bwd(scaling=8) == E.FP8L_EINVAL
+    assert bwd(rows=8) == E.FP8L_ESHAPE
+    for n in names:
+        if not n.endswith("am"):
+            assert bwd(**{n: None}) == E.FP8L_EINVAL, n
+    assert bwd(wsb=0) == E.FP8L_EWORKSPACE
+    for n in ("dh", "a", "b", "da", "db", "daq", "dbqt", "ws"):
+        assert bwd(**{n: A_BAD}) == E.FP8L_EALIGN, n
+    assert bwd(dbam=A16 + 1) == E.FP8L_EALIGN
+
+    def acc(dyq=A16, sdy=A16, wtq=A16, swt=A16, M=16, N=16, K=16, scaling=0, gx=A16):
+        v = lambda x: P(x) if x else None
+        return L.fp8_linear_bwd_x_acc(v(dyq), v(sdy), v(wtq), v(swt), M, N, K, scaling, v(gx),
+                                      None)
+
+    assert acc(scaling=4) == E.FP8L_EINVAL
+    assert acc(K=20) == E.FP8L_ESHAPE
+    assert acc(gx=None) == E.FP8L_EINVAL
+    assert acc(swt=None) == E.FP8L_EINVAL
+    assert acc(gx=A_BAD) == E.FP8L_EALIGN
