@@ -75,7 +75,7 @@ __device__ __forceinline__ float scale_from_amax(float a) {
 constexpr int AM_TR = 64;
 constexpr int AM_TC = 256;
 constexpr int AM_THREADS = 256;
-constexpr int TW_MAX_BLOCKS = 512;
+constexpr int TW_MAX_BLOCKS = 2048;
 
 // per-half maxima of two u16 pairs
 __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {

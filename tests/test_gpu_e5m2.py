@@ -99,14 +99,18 @@ def test_bwd_e5m2(mnk, rowwise):
     g32 = ops.fp8_linear_bwd_w_f32(qdy.qt, qdy.scale_t, qx.qt, qx.scale_t, M, N, K, rowwise,
                                    e5m2=True)
     torch.cuda.synchronize()
-    h = {k: G.host(v) for k, v in dict(dyq=qdy.q, sdy=qdy.scale, dytq=qdy.qt, sdyt=qdy.scale_t,
-                                       wtq=qw.qt, swt=qw.scale_t, xtq=qx.qt,
-                                       sxt=qx.scale_t).items()}
-    ox = oracle.gemm_tn_mixed(h["dyq"], 1, h["sdy"], h["wtq"], 0, h["swt"])
-    G.gemm_parity(G.host(gx), ox, h["dyq"], h["wtq"], h["sdy"], h["swt"],
+    # the oracle's own codes (equal to the device's, checked first)
+    rdy = oracle.quantize_e5m2(dy, rowwise)
+    rx = oracle.quantize(x, rowwise)
+    rw_ = oracle.quantize(w, rowwise)
+    for name, qz, r in (("dY", qdy, rdy), ("X", qx, rx), ("W", qw, rw_)):
+        G.assert_quantize_equal((G.host(qz.q), G.host(qz.qt), G.host(qz.scale),
+                                 G.host(qz.scale_t), G.host(qz.amax)), r, name)
+    ox = oracle.gemm_tn_mixed(rdy[0], 1, rdy[2], rw_[1], 0, rw_[3])
+    G.gemm_parity(G.host(gx), ox, rdy[0], rw_[1], rdy[2], rw_[3],
                   label="e5m2 grad_x %s" % (mnk,), e5m2_a=True)
-    ow = oracle.gemm_tn_mixed(h["dytq"], 1, h["sdyt"], h["xtq"], 0, h["sxt"])
-    G.gemm_parity(G.host(gw), ow, h["dytq"], h["xtq"], h["sdyt"], h["sxt"],
+    ow = oracle.gemm_tn_mixed(rdy[1], 1, rdy[3], rx[1], 0, rx[3])
+    G.gemm_parity(G.host(gw), ow, rdy[1], rx[1], rdy[3], rx[3],
                   label="e5m2 grad_w %s" % (mnk,), e5m2_a=True)
     bits = torch.from_numpy(G.host(g32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(bits, G.host(gw))

@@ -111,6 +111,16 @@ def _f32_parity(g, o, a, b, sa, sb, ii, jj, label):
     assert not bad.any(), "%s: %d elements outside the bound" % (label, int(bad.sum()))
 
 
+def _oracle_codes(x, dy, qx, qdy, rowwise):
+    """The oracle's quantize of x and dy, checked equal to the device's."""
+    rx = oracle.quantize(x, rowwise)
+    rdy = oracle.quantize(dy, rowwise)
+    for name, qz, r in (("X", qx, rx), ("dY", qdy, rdy)):
+        G.assert_quantize_equal((G.host(qz.q), G.host(qz.qt), G.host(qz.scale),
+                                 G.host(qz.scale_t), G.host(qz.amax)), r, name)
+    return rx, rdy
+
+
 @pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
 @pytest.mark.parametrize("mnk", [(272, 400, 528), (256, 256, 16), (1040, 784, 304)],
                          ids=lambda s: "%dx%dx%d" % s)
@@ -126,7 +136,8 @@ def test_bwd_w_f32(mnk, rowwise):
     _, g16 = ops.fp8_linear_bwd(None, None, qdy.qt, qdy.scale_t, None, None, qx.qt, qx.scale_t,
                                 M, N, K, rowwise, want_x=False)
     torch.cuda.synchronize()
-    a, sa, b, sb = G.host(qdy.qt), G.host(qdy.scale_t), G.host(qx.qt), G.host(qx.scale_t)
+    rx, rdy = _oracle_codes(x, dy, qx, qdy, rowwise)
+    a, sa, b, sb = rdy[1], rdy[3], rx[1], rx[3]
     o = oracle.gemm_tn_f32(a, sa, b, sb)
     ii, jj = np.divmod(np.arange(N * K), K)
     gh = G.host(g32)
@@ -154,7 +165,8 @@ def test_bwd_w_f32_full_size(rowwise):
     gh = G.host(g32)
     bits = torch.from_numpy(gh).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(bits, G.host(g16).view(np.uint16))
-    a, sa, b, sb = G.host(qdy.qt), G.host(qdy.scale_t), G.host(qx.qt), G.host(qx.scale_t)
+    rx, rdy = _oracle_codes(data["x"], data["dy"], qx, qdy, rowwise)
+    a, sa, b, sb = rdy[1], rdy[3], rx[1], rx[3]
     ii, jj = G.sample_indices(N, K, 6000, 45)
     o = oracle.gemm_tn_f32_sampled(a, sa, b, sb, ii, jj)
     _f32_parity(gh[ii, jj], o, a, b, sa, sb, ii, jj, "bwd_w_f32 full rowwise %s" % rowwise)
