@@ -3,13 +3,15 @@
 One step = the whole path for every linear of the workload: quantize X, W
 and dY (amax, scale, saturating E4M3 cast with the transposed copy), the
 forward GEMM and both backward GEMMs, all on device-resident synthetic
-inputs (seeded, Llama-3.1-shaped).  The default workload is the Llama-3.1-8B
+inputs (seeded, Llama-3.1-shaped), on one stream.  The default workload is the Llama-3.1-8B
 SwiGLU FFN (w1 and w3: X[8192x4096].W[14336x4096]^T, w2:
 X[8192x14336].W[4096x14336]^T), tensorwise scaling.
 
 Prints one JSON line: whole-step TFLOP/s (6*M*N*K per linear), the roofline
 of the dominant kernel (the fp8 GEMM, against the dense fp8 MFMA peak)
-measured with HIP events on the launch stream during the timed steps, the
+measured with HIP events on the launch stream around each linear's three
+GEMM launches during the timed steps (grouped: an event pair around every
+launch cost about 2% of the step), the
 same for the quantize chain against HBM bandwidth, and the CPU oracle timed
 on a bounded sample on the host cores.
 """
@@ -155,13 +157,43 @@ def measure_e5m2_step(steps, flops_per_step: int, reps: int = 10):
             "ms_per_step": round(el * 1e3 / reps, 4)}
 
 
+def measure_pipelined(steps, flops_per_step: int, stream, reps: int = 20):
+    """The whole step with each linear's quantizes on a side stream ahead of
+    the GEMMs (ops.PipelinedStep): wall time bracketed by device
+    synchronisation, then the GEMM groups' event time in further steps (the
+    GEMMs share the chip with the next linear's quantizes there)."""
+    import torch
+    from float8_mixed_precision_amd import ops
+    pipe = ops.PipelinedStep(steps, stream)
+    for _ in range(3):
+        pipe.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        pipe.run()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    rec = []
+    for _ in range(5):
+        rec += pipe.run(record=True)
+    torch.cuda.synchronize()
+    g = [(w, n, a.elapsed_time(b)) for k, n, w, a, b in rec if k == "gemm"]
+    gt = sum(w for w, _, _ in g) / (sum(t for _, _, t in g) * 1e-3) / 1e12
+    return {"metric": "whole step, quantizes of the next linear overlapping the GEMMs",
+            "value": round(flops_per_step * reps / el / 1e12, 2), "unit": "TFLOP/s",
+            "steps": reps, "ms_per_step": round(el * 1e3 / reps, 4),
+            "gemm_achieved_tflops": round(gt, 2), "gemm_frac": round(gt / PEAK_FP8_TFLOPS, 4),
+            "gemm_avg_launch_us": round(sum(t for _, _, t in g) * 1e3 / sum(n for _, n, _ in g), 2)}
+
+
 def measure_ffn_block(steps, wl, stream, reps: int = 5, e5m2_grad: bool = False):
     """The SwiGLU feed-forward block on the FFN workload's tensors (x and W1
     of w1, W3 of w3, W2 and dY of w2): x quantized once for w1 and w3, the
-    SwiGLU producers with the amax of h, da, db fused in, nine GEMMs.  Wall
-    time per step bracketed by device synchronisation; HIP events on the
-    launch stream around every launch for the split and the SwiGLU entry
-    points' bandwidth."""
+    SwiGLU producers with the amax of h, da, db fused in, nine GEMMs, on one
+    stream (the quantizes of the weights and of dY on a side stream measured
+    slower: they take power from the GEMMs).  Wall time per step bracketed
+    by device synchronisation; HIP events around every launch in further
+    steps for the split and the SwiGLU entry points' bandwidth."""
     import torch
     from float8_mixed_precision_amd import ops
 
@@ -179,15 +211,10 @@ def measure_ffn_block(steps, wl, stream, reps: int = 5, e5m2_grad: bool = False)
         blk.run()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / reps
+    # per-launch events, in further steps
     rec = []
     for _ in range(reps):
-        for kind, work, fn in blk.ops():
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            rec.append((kind, work, fn, e0, e1))
+        rec += [(k, w, None, a, b) for k, w, a, b in blk.run(record=True)]
     torch.cuda.synchronize()
     split = {}
     for kind in ("gemm", "quantize", "swiglu"):
@@ -309,35 +336,26 @@ def main():
         print(json.dumps(measure_ffn_block(steps, wl, stream, reps=args.steps)), flush=True)
         return
 
-    # per-op events: (kind, flops or bytes, start, end)
+    # one step: each linear's quantizes, then its GEMMs, on the current
+    # stream; timing events around each linear's group of three quantizes
+    # and group of three GEMMs, (kind, launches, work, start, end)
     def run_step(record):
-        evs = []
+        groups = []
         for ls in steps:
-            M, N, K, rw = ls.M, ls.N, ls.K, ls.rowwise
-            ops_list = (
-                ("quantize", 6 * M * K, lambda: ops.fp8_linear_quantize(ls.x, rw, ls.qx, ls.ws)),
-                ("quantize", 6 * N * K, lambda: ops.fp8_linear_quantize(ls.w, rw, ls.qw, ls.ws)),
-                ("quantize", 6 * M * N, lambda: ops.fp8_linear_quantize(ls.dy, rw, ls.qdy, ls.ws)),
-                ("gemm", 2 * M * N * K, lambda: ops.fp8_linear_fwd(
-                    ls.qx.q, ls.qx.scale, ls.qw.q, ls.qw.scale, rw, ls.out)),
-                ("gemm", 2 * M * N * K, lambda: ops.fp8_linear_bwd(
-                    ls.qdy.q, ls.qdy.scale, None, None, ls.qw.qt, ls.qw.scale_t, None, None,
-                    M, N, K, rw, grad_x=ls.grad_x, want_w=False)),
-                ("gemm", 2 * M * N * K, lambda: ops.fp8_linear_bwd(
-                    None, None, ls.qdy.qt, ls.qdy.scale_t, None, None, ls.qx.qt, ls.qx.scale_t,
-                    M, N, K, rw, grad_w=ls.grad_w, want_x=False)),
-            )
-            for kind, work, fn in ops_list:
+            for kind, work, fn in (
+                    ("quantize", 6 * (ls.M * ls.K + ls.N * ls.K + ls.M * ls.N),
+                     lambda: ls.quantize(stream)),
+                    ("gemm", 6 * ls.M * ls.N * ls.K, lambda: ls.gemms(stream))):
                 if record:
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record(stream)
                     fn()
                     e1.record(stream)
-                    evs.append((kind, work, e0, e1))
+                    groups.append((kind, 3, work, e0, e1))
                 else:
                     fn()
-        return evs
+        return groups
 
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -354,9 +372,9 @@ def main():
     elapsed = time.perf_counter() - t0
 
     def agg(kind):
-        work = sum(w for k, w, _, _ in all_evs if k == kind)
-        ms = sum(a.elapsed_time(b) for k, _, a, b in all_evs if k == kind)
-        n = sum(1 for k, _, _, _ in all_evs if k == kind)
+        work = sum(w for k, _, w, _, _ in all_evs if k == kind)
+        ms = sum(a.elapsed_time(b) for k, _, _, a, b in all_evs if k == kind)
+        n = sum(c for k, c, _, _, _ in all_evs if k == kind)
         return work, ms, n
 
     g_flops, g_ms, g_n = agg("gemm")
@@ -407,6 +425,8 @@ def main():
         print("[bench] next rows", file=sys.stderr, flush=True)
         result["next_rows"] = measure_next_rows(steps, stream)
         result["next_rows"]["e5m2_grad_step"] = measure_e5m2_step(steps, wl.flops)
+        print("[bench] pipelined step", file=sys.stderr, flush=True)
+        result["next_rows"]["pipelined_step"] = measure_pipelined(steps, wl.flops, stream)
         print("[bench] ffn block", file=sys.stderr, flush=True)
         blk = measure_ffn_block(steps, wl, stream)
         if blk is not None:

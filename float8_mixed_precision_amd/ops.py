@@ -372,13 +372,65 @@ class LinearStep:
         self.gemms(stream)
 
 
+class PipelinedStep:
+    """The linears of one step with their quantizes on a side stream.
+
+    The GEMMs are compute-bound and the quantizes bandwidth-bound, and the
+    quantizes of linear i+1 do not depend on the GEMMs of linear i: they are
+    issued on ``side`` (a second stream at the default priority) ahead of
+    the GEMMs on ``main``.  Ordering: ``run()`` first makes the side stream
+    wait for all work already issued on ``main`` (so inputs written there,
+    and the previous step's GEMMs that read the fp8 copies, come first);
+    linear i's GEMMs wait for its quantizes.  The results are those of
+    running each LinearStep in turn on ``main``.
+
+    ``run(record=True)`` also brackets each linear's quantize group and
+    GEMM group with timing events and returns (kind, launches, work, start,
+    end) per group: kind "quantize" (3 quantizes, work = bytes) or "gemm"
+    (fwd, grad_x, grad_w; work = flops).
+    """
+
+    def __init__(self, steps, main=None, side=None):
+        self.steps = list(steps)
+        self.main = main if main is not None else torch.cuda.current_stream()
+        self.side = side if side is not None else torch.cuda.Stream(device=self.main.device)
+        self.start = torch.cuda.Event()
+        self.q_done = [torch.cuda.Event() for _ in self.steps]
+
+    def run(self, record: bool = False):
+        groups = []
+
+        def timed(kind, n, work, stream, fn):
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                groups.append((kind, n, work, e0, e1))
+            else:
+                fn()
+
+        self.start.record(self.main)
+        self.side.wait_event(self.start)
+        for i, ls in enumerate(self.steps):
+            qbytes = 6 * (ls.M * ls.K + ls.N * ls.K + ls.M * ls.N)
+            timed("quantize", 3, qbytes, self.side, lambda: ls.quantize(self.side))
+            self.q_done[i].record(self.side)
+        for i, ls in enumerate(self.steps):
+            self.main.wait_event(self.q_done[i])
+            timed("gemm", 3, 6 * ls.M * ls.N * ls.K, self.main, lambda: ls.gemms(self.main))
+        return groups
+
+
 # ------------------------------------------------------ SwiGLU FFN block --
 
 class SwiGLUFFNStep:
     """One Float8 SwiGLU feed-forward block fwd+bwd on preallocated buffers.
 
     x [M, D], w1 and w3 [H, D], w2 [D, H], d_out [M, D] (bf16).  ``run()``
-    enqueues, on the current stream:
+    enqueues, on the current stream (the quantizes of the weights and of
+    d_out on ``side`` when a second stream is given):
 
       quantize x once (read by w1 and w3), quantize w1, w3, w2
       a = x.w1^T, b = x.w3^T                       (fp8 GEMMs)
@@ -413,7 +465,10 @@ class SwiGLUFFNStep:
         ws = max(fp8_linear_workspace_bytes(r, c, rowwise) for r, c in
                  ((M, D), (H, D), (D, H)))
         self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.ws_side = torch.zeros_like(self.ws)     # quantizes on a second stream
         self.ws_sw = alloc_swiglu_workspace(M, H, rowwise, dev)
+        self._start = torch.cuda.Event()
+        self._side_events = {n: torch.cuda.Event() for n in ("qw1", "qw3", "qw2", "qdy")}
         self.a = torch.empty((M, H), **bf)
         self.b = torch.empty((M, H), **bf)
         self.h = torch.empty((M, H), **bf)
@@ -432,58 +487,98 @@ class SwiGLUFFNStep:
         return 18 * self.M * self.D * self.H
 
     def ops(self):
-        """The launches of one step, in order: (kind, work, fn) with kind one
-        of "quantize", "swiglu", "gemm" and work the algorithmic bytes
-        (quantize / swiglu) or flops (gemm) of the launch."""
+        """The launches of one step, in order: (name, kind, work, side,
+        needs, fn) with kind one of "quantize", "swiglu", "gemm"; work the
+        algorithmic bytes (quantize / swiglu) or flops (gemm) of the launch;
+        side True for the launches that depend on no other launch of the
+        step (the quantizes of the weights and of d_out); needs the names
+        of the side launches this one reads; fn(stream) the call."""
         M, D, H, rw, e5 = self.M, self.D, self.H, self.rowwise, self.e5m2_grad
         g = 2 * M * D * H
         return (
-            ("quantize", 6 * M * D, lambda: fp8_linear_quantize(self.x, rw, self.qx, self.ws)),
-            ("quantize", 6 * H * D, lambda: fp8_linear_quantize(self.w1, rw, self.qw1, self.ws)),
-            ("quantize", 6 * H * D, lambda: fp8_linear_quantize(self.w3, rw, self.qw3, self.ws)),
-            ("quantize", 6 * D * H, lambda: fp8_linear_quantize(self.w2, rw, self.qw2, self.ws)),
-            ("gemm", g, lambda: fp8_linear_fwd(self.qx.q, self.qx.scale, self.qw1.q,
-                                               self.qw1.scale, rw, self.a)),
-            ("gemm", g, lambda: fp8_linear_fwd(self.qx.q, self.qx.scale, self.qw3.q,
-                                               self.qw3.scale, rw, self.b)),
+            ("qw1", "quantize", 6 * H * D, True, (),
+             lambda st: fp8_linear_quantize(self.w1, rw, self.qw1, self.ws_side, st)),
+            ("qw3", "quantize", 6 * H * D, True, (),
+             lambda st: fp8_linear_quantize(self.w3, rw, self.qw3, self.ws_side, st)),
+            ("qw2", "quantize", 6 * D * H, True, (),
+             lambda st: fp8_linear_quantize(self.w2, rw, self.qw2, self.ws_side, st)),
+            ("qdy", "quantize", 6 * M * D, True, (),
+             lambda st: fp8_linear_quantize(self.d_out, rw, self.qdy, self.ws_side, st,
+                                            e5m2=e5)),
+            ("qx", "quantize", 6 * M * D, False, (),
+             lambda st: fp8_linear_quantize(self.x, rw, self.qx, self.ws, st)),
+            ("a", "gemm", g, False, ("qw1",),
+             lambda st: fp8_linear_fwd(self.qx.q, self.qx.scale, self.qw1.q, self.qw1.scale, rw,
+                                       self.a, st)),
+            ("b", "gemm", g, False, ("qw3",),
+             lambda st: fp8_linear_fwd(self.qx.q, self.qx.scale, self.qw3.q, self.qw3.scale, rw,
+                                       self.b, st)),
             # a, b read twice (elementwise pass, then h read by the cast),
             # h written once; q and qt written
-            ("swiglu", 10 * M * H, lambda: fp8_swiglu_fwd(self.a, self.b, rw, self.h, self.qh,
-                                                          self.ws_sw)),
-            ("gemm", g, lambda: fp8_linear_fwd(self.qh.q, self.qh.scale, self.qw2.q,
-                                               self.qw2.scale, rw, self.out)),
-            ("quantize", 6 * M * D, lambda: fp8_linear_quantize(self.d_out, rw, self.qdy,
-                                                                self.ws, e5m2=e5)),
-            ("gemm", g, lambda: fp8_linear_bwd(self.qdy.q, self.qdy.scale, None, None,
-                                               self.qw2.qt, self.qw2.scale_t, None, None,
-                                               M, D, H, rw, grad_x=self.dh, want_w=False,
-                                               e5m2=e5)),
-            ("gemm", g, lambda: fp8_linear_bwd(None, None, self.qdy.qt, self.qdy.scale_t,
-                                               None, None, self.qh.qt, self.qh.scale_t,
-                                               M, D, H, rw, grad_w=self.grad_w2, want_x=False,
-                                               e5m2=e5)),
+            ("swiglu_fwd", "swiglu", 10 * M * H, False, (),
+             lambda st: fp8_swiglu_fwd(self.a, self.b, rw, self.h, self.qh, self.ws_sw, st)),
+            ("out", "gemm", g, False, ("qw2",),
+             lambda st: fp8_linear_fwd(self.qh.q, self.qh.scale, self.qw2.q, self.qw2.scale, rw,
+                                       self.out, st)),
+            ("dh", "gemm", g, False, ("qw2", "qdy"), lambda st: fp8_linear_bwd(
+                self.qdy.q, self.qdy.scale, None, None, self.qw2.qt, self.qw2.scale_t, None,
+                None, M, D, H, rw, grad_x=self.dh, want_w=False, stream=st, e5m2=e5)),
+            ("grad_w2", "gemm", g, False, ("qdy",), lambda st: fp8_linear_bwd(
+                None, None, self.qdy.qt, self.qdy.scale_t, None, None, self.qh.qt,
+                self.qh.scale_t, M, D, H, rw, grad_w=self.grad_w2, want_x=False, stream=st,
+                e5m2=e5)),
             # dh, a, b read; da, db written; each read again by its cast,
             # whose q and qt are written
-            ("swiglu", 18 * M * H, lambda: fp8_swiglu_bwd(self.dh, self.a, self.b, rw, self.da,
-                                                          self.db, self.qda, self.qdb,
-                                                          self.ws_sw, e5m2=e5)),
-            ("gemm", g, lambda: fp8_linear_bwd(self.qda.q, self.qda.scale, None, None,
-                                               self.qw1.qt, self.qw1.scale_t, None, None,
-                                               M, H, D, rw, grad_x=self.grad_x, want_w=False,
-                                               e5m2=e5)),
-            ("gemm", g, lambda: fp8_linear_bwd_x_acc(self.qdb.q, self.qdb.scale, self.qw3.qt,
-                                                     self.qw3.scale_t, M, H, D, self.grad_x,
-                                                     rw, e5m2=e5)),
-            ("gemm", g, lambda: fp8_linear_bwd(None, None, self.qda.qt, self.qda.scale_t,
-                                               None, None, self.qx.qt, self.qx.scale_t,
-                                               M, H, D, rw, grad_w=self.grad_w1, want_x=False,
-                                               e5m2=e5)),
-            ("gemm", g, lambda: fp8_linear_bwd(None, None, self.qdb.qt, self.qdb.scale_t,
-                                               None, None, self.qx.qt, self.qx.scale_t,
-                                               M, H, D, rw, grad_w=self.grad_w3, want_x=False,
-                                               e5m2=e5)),
+            ("swiglu_bwd", "swiglu", 18 * M * H, False, (),
+             lambda st: fp8_swiglu_bwd(self.dh, self.a, self.b, rw, self.da, self.db, self.qda,
+                                       self.qdb, self.ws_sw, st, e5m2=e5)),
+            ("grad_x", "gemm", g, False, ("qw1",), lambda st: fp8_linear_bwd(
+                self.qda.q, self.qda.scale, None, None, self.qw1.qt, self.qw1.scale_t, None,
+                None, M, H, D, rw, grad_x=self.grad_x, want_w=False, stream=st, e5m2=e5)),
+            ("grad_x_acc", "gemm", g, False, ("qw3",), lambda st: fp8_linear_bwd_x_acc(
+                self.qdb.q, self.qdb.scale, self.qw3.qt, self.qw3.scale_t, M, H, D,
+                self.grad_x, rw, st, e5m2=e5)),
+            ("grad_w1", "gemm", g, False, (), lambda st: fp8_linear_bwd(
+                None, None, self.qda.qt, self.qda.scale_t, None, None, self.qx.qt,
+                self.qx.scale_t, M, H, D, rw, grad_w=self.grad_w1, want_x=False, stream=st,
+                e5m2=e5)),
+            ("grad_w3", "gemm", g, False, (), lambda st: fp8_linear_bwd(
+                None, None, self.qdb.qt, self.qdb.scale_t, None, None, self.qx.qt,
+                self.qx.scale_t, M, H, D, rw, grad_w=self.grad_w3, want_x=False, stream=st,
+                e5m2=e5)),
         )
 
-    def run(self):
-        for _, _, fn in self.ops():
-            fn()
+    def run(self, side=None, record: bool = False):
+        """Enqueue one step on the current stream.  With ``side`` (a second
+        stream) the launches marked side run there, after all work already
+        issued on the current stream, and each launch on the current stream
+        first waits for the side launches it reads; the results are those of
+        the single-stream order.  record: timing events around every launch,
+        returned as (kind, work, start, end)."""
+        main = torch.cuda.current_stream()
+        if side is not None:
+            self._start.record(main)
+            side.wait_event(self._start)
+        rec = []
+        done = {}
+        for name, kind, work, on_side, needs, fn in self.ops():
+            st = side if (on_side and side is not None) else main
+            for n in needs:
+                if n in done:
+                    main.wait_event(done.pop(n))
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                fn(st)
+                e1.record(st)
+                rec.append((kind, work, e0, e1))
+            else:
+                fn(st)
+            if st is not main:
+                ev = self._side_events[name]
+                ev.record(st)
+                done[name] = ev
+        for ev in done.values():      # the step ends with the side stream joined
+            main.wait_event(ev)
+        return rec

@@ -77,3 +77,37 @@ def test_rowwise_at_headline_shape_with_gaussian_inputs():
     lin = wl.linears[0]
     data = W.generate_linear(wl, 0)
     check_linear(lin, data, True, sampled=True, seed=9)
+
+
+def test_pipelined_step_equals_serial():
+    """PipelinedStep (quantizes on a side stream) gives the outputs of the
+    linears run in turn, also when the inputs change between steps on the
+    main stream."""
+    shapes = ((512, 1024, 256), (512, 1024, 256), (512, 256, 1024))
+
+    def make(seed):
+        x = G.dev_bf16(W.random_bf16(seed, (512, 256), 1.0, 0))
+        ins = []
+        for li, (M, N, K) in enumerate(shapes):
+            xx = x if K == 256 else G.dev_bf16(W.random_bf16(seed, (M, K), 1.0, 10 + li))
+            ins.append((xx, G.dev_bf16(W.random_bf16(seed, (N, K), 0.02, 20 + li)),
+                        G.dev_bf16(W.random_bf16(seed, (M, N), 1e-2, 30 + li))))
+        return ins
+    a, b = make(71), make(72)
+    steps = [ops.LinearStep(x.clone(), w.clone(), dy.clone()) for x, w, dy in a]
+    pipe = ops.PipelinedStep(steps)
+    got = []
+    for ins in (a, b):
+        for ls, (x, w, dy) in zip(steps, ins):     # new inputs, written on the main stream
+            ls.x.copy_(x); ls.w.copy_(w); ls.dy.copy_(dy)
+        G.say("pipelined step")
+        pipe.run()
+        got.append([t.clone() for ls in steps for t in (ls.out, ls.grad_x, ls.grad_w)])
+    torch.cuda.synchronize()
+    for ins, g in zip((a, b), got):
+        ref = [ops.LinearStep(x, w, dy) for x, w, dy in ins]
+        for r in ref:
+            r.run()
+        torch.cuda.synchronize()
+        want = [t for r in ref for t in (r.out, r.grad_x, r.grad_w)]
+        assert all(torch.equal(p, q) for p, q in zip(g, want))

@@ -283,8 +283,15 @@ def test_ffn_block(rowwise, e5m2):
     blk = ops.SwiGLUFFNStep(*[G.dev_bf16(t) for t in (x, w1, w3, w2, dy)], rowwise=rowwise,
                             e5m2_grad=e5m2)
     blk.run()
-    blk.run()           # a second step over the same buffers gives the same result
     torch.cuda.synchronize()
+    names = ("a", "b", "h", "out", "dh", "grad_w2", "da", "db", "grad_x", "grad_w1", "grad_w3")
+    single = {n: G.host(getattr(blk, n)) for n in names}
+    # a second step over the same buffers, with the independent quantizes on
+    # a side stream, gives the same result
+    blk.run(torch.cuda.Stream(device=G.DEV))
+    torch.cuda.synchronize()
+    for n in names:
+        assert np.array_equal(G.host(getattr(blk, n)), single[n]), "side stream: %s" % n
     ref = _oracle_block(x, w1, w3, w2, dy, rowwise, e5m2)
     for name, qz in (("qx", blk.qx), ("q1", blk.qw1), ("q3", blk.qw3), ("q2", blk.qw2)):
         G.assert_quantize_equal(_host_q(qz), ref[name], name)
