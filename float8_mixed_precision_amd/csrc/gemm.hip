@@ -87,6 +87,12 @@ constexpr int GROUP_M = 4;
 constexpr int NUM_XCD = 8;
 constexpr uint32_t OOB = 0x80000000u;    // operand offset that reads as zero
 constexpr uint32_t OOB_C = 0xFFFFFF00u;  // output offset that is dropped
+// Cache policy of the output stores: non-temporal ("nt").  The output is not
+// read again by the GEMM, and streaming it out keeps it from evicting the
+// operand panels from L2 and from leaving dirty lines in the Infinity Cache
+// that the next kernel would have to write back (measured: the GEMMs of the
+// FFN step 3% faster, the amax passes after them faster too).
+constexpr int C_STORE_AUX = 2;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
         for (int u = 0; u < 8; ++u) {
           const int row = frow0 + (it0 + u) * 2;
           const uint32_t off = (fcol_ok && row < M) ? (uint32_t)((row * N + fcol) * 4) : OOB_C;
-          __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off, 0, C_STORE_AUX);
         }
       }
     }
@@ -520,7 +526,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off[u], 0, 0);
+    for (int u = 0; u < 8; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off[u], 0, C_STORE_AUX);
   }
 }
 
