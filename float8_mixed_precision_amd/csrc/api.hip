@@ -164,6 +164,35 @@ int fp8_linear_bwd_w_f32(const void *dytq, const float *sdyt, const void *xtq,
   return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
 }
 
+int fp8_linear_gemm_grouped(const fp8l_gemm_problem *problems, int count, int scaling,
+                            void *stream) {
+  if (!problems || count < 1 || count > FP8L_MAX_GROUP) return FP8L_EINVAL;
+  if (bad_scaling(scaling)) return FP8L_EINVAL;
+  fp8l::GemmDesc d[FP8L_MAX_GROUP];
+  for (int i = 0; i < count; ++i) {
+    const fp8l_gemm_problem &p = problems[i];
+    if (bad_dim(p.m) || bad_dim(p.n) || bad_dim(p.k)) return FP8L_ESHAPE;
+    if (bad_gemm_sizes(p.m, p.n, p.k)) return FP8L_ESHAPE;
+    int s = check_gemm_operands(p.a, p.sa, p.b, p.sb, p.c, p.m, p.n, p.k);
+    if (s != FP8L_OK) return s;
+    d[i] = {static_cast<const uint8_t *>(p.a), p.sa, static_cast<const uint8_t *>(p.b), p.sb,
+            p.c, p.m, p.n, p.k};
+  }
+  // outputs pairwise disjoint
+  for (int i = 0; i < count; ++i)
+    for (int j = i + 1; j < count; ++j) {
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(problems[i].c);
+      const uintptr_t a1 = a0 + (uintptr_t)(2 * problems[i].m * problems[i].n);
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(problems[j].c);
+      const uintptr_t b1 = b0 + (uintptr_t)(2 * problems[j].m * problems[j].n);
+      if (a0 < b1 && b0 < a1) return FP8L_EINVAL;
+    }
+  hipError_t e = fp8l::gemm_group_launch(d, count, (scaling & FP8L_ROWWISE) != 0,
+                                         (scaling & FP8L_E5M2) != 0,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
 int fp8_linear_bwd_x_acc(const void *dyq, const float *sdy, const void *wtq, const float *swt,
                          int64_t M, int64_t N, int64_t K, int scaling, void *grad_x,
                          void *stream) {

@@ -168,6 +168,18 @@ hipError_t swiglu_bwd_launch(const void *dh, const void *a, const void *b, int64
 hipError_t gemm_launch(const uint8_t *A, const float *sa, const uint8_t *B,
                        const float *sb, int rowwise, int fmt_a, int64_t M, int64_t N,
                        int64_t K, uint16_t *C, hipStream_t stream);
+// Several such GEMMs (bf16 outputs, same scaling and format of A) in one
+// launch; count 1..4.
+struct GemmDesc {
+  const uint8_t *A;
+  const float *sa;
+  const uint8_t *B;
+  const float *sb;
+  void *C;
+  int64_t M, N, K;
+};
+hipError_t gemm_group_launch(const GemmDesc *d, int count, int rowwise, int fmt_a,
+                             hipStream_t stream);
 // The same GEMM added into C: C = bf16(fl32(C) + fl32(bf16 GEMM result)).
 hipError_t gemm_acc_launch(const uint8_t *A, const float *sa, const uint8_t *B,
                            const float *sb, int rowwise, int fmt_a, int64_t M, int64_t N,

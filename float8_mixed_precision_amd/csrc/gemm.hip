@@ -150,6 +150,35 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m,
   tn = in_group / gm;
 }
 
+// Up to MAX_GROUP GEMMs of one variant in one launch: problem i owns the
+// workgroups [first[i], first[i] + tiles_m[i] * tiles_n[i]).  A grid whose
+// last round of tiles would leave CUs idle (896 tiles on 256 CUs) can share
+// that round with another problem.  first[i] is a multiple of 8 whenever
+// the problems before it have a multiple of 8 tiles, which keeps the XCD
+// mapping of tile_of_block.
+constexpr int MAX_GROUP = 4;
+struct GemmGroup {
+  const uint8_t *A[MAX_GROUP];
+  const float *sa[MAX_GROUP];
+  const uint8_t *B[MAX_GROUP];
+  const float *sb[MAX_GROUP];
+  void *C[MAX_GROUP];
+  int M[MAX_GROUP], N[MAX_GROUP], K[MAX_GROUP];
+  int tiles_m[MAX_GROUP], tiles_n[MAX_GROUP], first[MAX_GROUP];
+  int count;
+};
+
+// element i of a kernel-argument array for a wave-uniform i (selects, so the
+// array is never copied to private memory)
+template <class T>
+__device__ __forceinline__ T pick(const T (&v)[MAX_GROUP], int i) {
+  T r = v[0];
+#pragma unroll
+  for (int k = 1; k < MAX_GROUP; ++k)
+    if (i == k) r = v[k];
+  return r;
+}
+
 // KFULL: K % 128 == 0 (no K tail, no per-chunk K check).  RW: rowwise
 // scales (sa[M], sb[N]) instead of one scale per operand.  F32: fp32 output
 // (the scaled value before bf16 rounding) instead of bf16.  FA: code format
@@ -159,12 +188,22 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m,
 // entry and receives bf16(fl32(C) + fl32(bf16 result)), the sum of two
 // gradient contributions as bf16 tensors add.
 template <bool KFULL, bool RW, bool F32, int FA, bool ACC>
-__global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
-    const uint8_t *__restrict__ A, const float *__restrict__ sa,
-    const uint8_t *__restrict__ B, const float *__restrict__ sb,
-    int M, int N, int K, void *__restrict__ C, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(GemmGroup g) {
   static_assert(!(F32 && ACC), "accumulation is into a bf16 output");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[INV_OFF + (RW ? INV_BYTES : 0)];
+
+  // this workgroup's problem (uniform) and its block index within it
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < MAX_GROUP; ++i)
+    if (i < g.count && (int)blockIdx.x >= g.first[i]) pi = i;
+  const uint8_t *__restrict__ A = pick(g.A, pi);
+  const float *__restrict__ sa = pick(g.sa, pi);
+  const uint8_t *__restrict__ B = pick(g.B, pi);
+  const float *__restrict__ sb = pick(g.sb, pi);
+  void *__restrict__ C = pick(g.C, pi);
+  const int M = pick(g.M, pi), N = pick(g.N, pi), K = pick(g.K, pi);
+  const int tiles_m = pick(g.tiles_m, pi), tiles_n = pick(g.tiles_n, pi);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,7 +212,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
   const int wn = wave & 1;
 
   int tmi, tni;
-  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tmi, tni);
+  tile_of_block((int)blockIdx.x - pick(g.first, pi), tiles_m * tiles_n, tiles_m, tiles_n, tmi,
+                tni);
   const int m0 = tmi * BM;
   const int n0 = tni * BN;
 
@@ -534,22 +574,45 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(
 
 namespace {
 
+// One launch over the problems of d (count <= MAX_GROUP, bf16 or fp32
+// outputs per F32, accumulating per ACC); empty problems get no workgroups.
 template <bool F32, int FA, bool ACC = false>
-hipError_t launch_variant(const uint8_t *A, const float *sa, const uint8_t *B,
-                          const float *sb, int rowwise, int64_t M, int64_t N, int64_t K,
-                          void *C, hipStream_t stream) {
-  if (M == 0 || N == 0) return hipSuccess;
-  const int tiles_m = (int)((M + BM - 1) / BM);
-  const int tiles_n = (int)((N + BN - 1) / BN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
-  const bool kfull = K % BK == 0;
+hipError_t launch_group(const GemmDesc *d, int count, int rowwise, hipStream_t stream) {
+  GemmGroup g = {};
+  int blocks = 0;
+  bool kfull = true;
+  for (int i = 0; i < count; ++i) {
+    if (d[i].M == 0 || d[i].N == 0) continue;
+    const int c = g.count++;
+    g.A[c] = d[i].A;
+    g.sa[c] = d[i].sa;
+    g.B[c] = d[i].B;
+    g.sb[c] = d[i].sb;
+    g.C[c] = d[i].C;
+    g.M[c] = (int)d[i].M;
+    g.N[c] = (int)d[i].N;
+    g.K[c] = (int)d[i].K;
+    g.tiles_m[c] = (int)((d[i].M + BM - 1) / BM);
+    g.tiles_n[c] = (int)((d[i].N + BN - 1) / BN);
+    g.first[c] = blocks;
+    blocks += g.tiles_m[c] * g.tiles_n[c];
+    kfull = kfull && d[i].K % BK == 0;
+  }
+  if (blocks == 0) return hipSuccess;
   auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true, F32, FA, ACC>
                                : k_gemm_fp8_tn<false, true, F32, FA, ACC>)
                       : (kfull ? k_gemm_fp8_tn<true, false, F32, FA, ACC>
                                : k_gemm_fp8_tn<false, false, F32, FA, ACC>);
-  hipLaunchKernelGGL(kern, grid, dim3(THREADS), 0, stream, A, sa, B, sb, (int)M, (int)N,
-                     (int)K, C, tiles_m, tiles_n);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(THREADS), 0, stream, g);
   return hipGetLastError();
+}
+
+template <bool F32, int FA, bool ACC = false>
+hipError_t launch_variant(const uint8_t *A, const float *sa, const uint8_t *B,
+                          const float *sb, int rowwise, int64_t M, int64_t N, int64_t K,
+                          void *C, hipStream_t stream) {
+  const GemmDesc d = {A, sa, B, sb, C, M, N, K};
+  return launch_group<F32, FA, ACC>(&d, 1, rowwise, stream);
 }
 
 }  // namespace
@@ -566,6 +629,13 @@ hipError_t gemm_acc_launch(const uint8_t *A, const float *sa, const uint8_t *B,
                            int64_t K, uint16_t *C, hipStream_t stream) {
   return fmt_a ? launch_variant<false, 1, true>(A, sa, B, sb, rowwise, M, N, K, C, stream)
                : launch_variant<false, 0, true>(A, sa, B, sb, rowwise, M, N, K, C, stream);
+}
+
+hipError_t gemm_group_launch(const GemmDesc *d, int count, int rowwise, int fmt_a,
+                             hipStream_t stream) {
+  if (count < 1 || count > MAX_GROUP) return hipErrorInvalidValue;
+  return fmt_a ? launch_group<false, 1>(d, count, rowwise, stream)
+               : launch_group<false, 0>(d, count, rowwise, stream);
 }
 
 hipError_t gemm_f32_launch(const uint8_t *A, const float *sa, const uint8_t *B,

@@ -24,9 +24,20 @@ FP8L_OK, FP8L_EINVAL, FP8L_ESHAPE, FP8L_EALIGN, FP8L_EWORKSPACE, FP8L_EHIP = ran
 FP8L_TENSORWISE, FP8L_ROWWISE, FP8L_E5M2 = 0, 1, 2
 EXPORTS = ("fp8_linear_workspace_bytes", "fp8_linear_quantize", "fp8_linear_amax",
            "fp8_linear_quantize_scaled", "fp8_linear_fwd", "fp8_linear_bwd",
-           "fp8_linear_bwd_w_f32", "fp8_linear_bwd_x_acc", "fp8_linear_encode_e4m3",
+           "fp8_linear_bwd_w_f32", "fp8_linear_bwd_x_acc", "fp8_linear_gemm_grouped",
+           "fp8_linear_encode_e4m3",
            "fp8_linear_encode_e5m2", "fp8_swiglu_workspace_bytes", "fp8_swiglu_fwd",
            "fp8_swiglu_bwd", "fp8_linear_status_string", "fp8_linear_version")
+
+
+FP8L_MAX_GROUP = 4
+
+
+class GemmProblem(ctypes.Structure):
+    """fp8l_gemm_problem of the C ABI."""
+    _fields_ = [("a", ctypes.c_void_p), ("sa", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("sb", ctypes.c_void_p), ("c", ctypes.c_void_p), ("m", ctypes.c_int64),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
 
 
 class Fp8LinearError(RuntimeError):
@@ -62,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.fp8_linear_quantize_scaled.argtypes = [P, i64, i64, P, P, P, P]
     L.fp8_linear_bwd_w_f32.restype = I
     L.fp8_linear_bwd_w_f32.argtypes = [P, P, P, P, i64, i64, i64, I, P, P]
+    L.fp8_linear_gemm_grouped.restype = I
+    L.fp8_linear_gemm_grouped.argtypes = [ctypes.POINTER(GemmProblem), I, I, P]
     L.fp8_linear_bwd_x_acc.restype = I
     L.fp8_linear_bwd_x_acc.argtypes = [P, P, P, P, i64, i64, i64, I, P, P]
     L.fp8_swiglu_workspace_bytes.restype = ctypes.c_size_t
@@ -231,6 +244,21 @@ def fp8_linear_bwd_w_f32(dytq, sdyt, xtq, sxt, M: int, N: int, K: int,
     return grad_w
 
 
+def fp8_linear_gemm_grouped(problems, rowwise: bool = False, stream=None,
+                            e5m2: bool = False) -> None:
+    """One launch of up to FP8L_MAX_GROUP GEMMs c = (a . b^T) / (sa * sb):
+    problems is a sequence of (a [m, k], sa, b [n, k], sb, c [m, n] bf16)."""
+    arr = (GemmProblem * len(problems))()
+    for i, (a, sa, b, sb, c) in enumerate(problems):
+        m, k = a.shape
+        n = b.shape[0]
+        assert c.shape == (m, n) and c.dtype == torch.bfloat16
+        arr[i] = GemmProblem(a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
+                             c.data_ptr(), m, n, k)
+    _check(lib().fp8_linear_gemm_grouped(arr, len(problems), _scaling(rowwise, e5m2),
+                                         _stream(stream)), "fp8_linear_gemm_grouped")
+
+
 def fp8_linear_bwd_x_acc(dyq, sdy, wtq, swt, M: int, N: int, K: int, grad_x: torch.Tensor,
                          rowwise: bool = False, stream=None, e5m2: bool = False) -> torch.Tensor:
     """grad_x [M, K] (bf16, in place) = bf16(grad_x + bf16(dY . W)): the second
@@ -336,13 +364,17 @@ class LinearStep:
     """
 
     def __init__(self, x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor,
-                 rowwise: bool = False, e5m2_grad: bool = False):
+                 rowwise: bool = False, e5m2_grad: bool = False,
+                 qx: Optional[Quantized] = None):
         self.x, self.w, self.dy, self.rowwise = x, w, dy, rowwise
         self.e5m2_grad = e5m2_grad
         self.M, self.K = x.shape
         self.N = w.shape[0]
         dev = x.device
-        self.qx = alloc_quantized(self.M, self.K, rowwise, dev)
+        # qx given: X's quantize belongs to another linear reading the same
+        # X (w1 and w3 of the SwiGLU feed-forward), which runs it first
+        self.owns_qx = qx is None
+        self.qx = alloc_quantized(self.M, self.K, rowwise, dev) if qx is None else qx
         self.qw = alloc_quantized(self.N, self.K, rowwise, dev)
         self.qdy = alloc_quantized(self.M, self.N, rowwise, dev)
         ws = max(fp8_linear_workspace_bytes(self.M, self.K, rowwise),
@@ -353,8 +385,14 @@ class LinearStep:
         self.grad_x = torch.empty((self.M, self.K), dtype=torch.bfloat16, device=dev)
         self.grad_w = torch.empty((self.N, self.K), dtype=torch.bfloat16, device=dev)
 
+    @property
+    def quantize_bytes(self) -> int:
+        """Algorithmic bytes of quantize(): 6 per element of each tensor."""
+        return 6 * ((self.M * self.K if self.owns_qx else 0) + self.N * self.K + self.M * self.N)
+
     def quantize(self, stream=None):
-        fp8_linear_quantize(self.x, self.rowwise, self.qx, self.ws, stream)
+        if self.owns_qx:
+            fp8_linear_quantize(self.x, self.rowwise, self.qx, self.ws, stream)
         fp8_linear_quantize(self.w, self.rowwise, self.qw, self.ws, stream)
         fp8_linear_quantize(self.dy, self.rowwise, self.qdy, self.ws, stream,
                             e5m2=self.e5m2_grad)
@@ -367,9 +405,79 @@ class LinearStep:
                        self.M, self.N, self.K, self.rowwise, self.grad_x, self.grad_w,
                        stream=stream, e5m2=self.e5m2_grad)
 
+    def gemms_fwd_x(self, stream=None):
+        """The forward GEMM and grad_X (grad_W left to a grouped launch)."""
+        fp8_linear_fwd(self.qx.q, self.qx.scale, self.qw.q, self.qw.scale, self.rowwise,
+                       self.out, stream)
+        fp8_linear_bwd(self.qdy.q, self.qdy.scale, None, None, self.qw.qt, self.qw.scale_t,
+                       None, None, self.M, self.N, self.K, self.rowwise, grad_x=self.grad_x,
+                       want_w=False, stream=stream, e5m2=self.e5m2_grad)
+
+    def grad_w_problem(self):
+        """grad_W [N, K] = dY^T . X as a fp8_linear_gemm_grouped problem."""
+        return (self.qdy.qt, self.qdy.scale_t, self.qx.qt, self.qx.scale_t, self.grad_w)
+
     def run(self, stream=None):
         self.quantize(stream)
         self.gemms(stream)
+
+
+class GroupedStep:
+    """The linears of one step on one stream, with the grad_W GEMMs of
+    consecutive linears of the same grad_W shape in one grouped launch (two
+    896-tile grids fill the 256 compute units' last round together instead
+    of each leaving it half idle).  Per linear: its quantizes, the forward
+    GEMM and grad_X; then the grouped grad_W.  Same results as each
+    LinearStep's run() in turn.
+
+    ``run(record=True)`` brackets each linear's quantizes, its two GEMMs and
+    each grad_W launch with timing events and returns (kind, launches,
+    work, start, end) per group (kind "quantize" with work in bytes, or
+    "gemm" with work in flops and launches counting kernel dispatches).
+    """
+
+    def __init__(self, steps):
+        self.steps = list(steps)
+        shape = lambda ls: (ls.N, ls.K, ls.M, ls.rowwise, ls.e5m2_grad)
+        # pairs of consecutive linears with the same grad_W shape
+        self.plan = []          # ("x", i) for fwd + grad_x of i, ("w", [i, ...]) for grad_W
+        i = 0
+        while i < len(self.steps):
+            if i + 1 < len(self.steps) and shape(self.steps[i]) == shape(self.steps[i + 1]):
+                self.plan += [("x", i), ("x", i + 1), ("w", [i, i + 1])]
+                i += 2
+            else:
+                self.plan += [("x", i), ("w", [i])]
+                i += 1
+
+    def run(self, stream=None, record: bool = False):
+        st = stream if stream is not None else torch.cuda.current_stream()
+        groups = []
+
+        def timed(kind, n, work, fn):
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                fn()
+                e1.record(st)
+                groups.append((kind, n, work, e0, e1))
+            else:
+                fn()
+
+        for kind, arg in self.plan:
+            if kind == "x":
+                ls = self.steps[arg]
+                timed("quantize", 3 if ls.owns_qx else 2, ls.quantize_bytes,
+                      lambda: ls.quantize(st))
+                timed("gemm", 2, 4 * ls.M * ls.N * ls.K, lambda: ls.gemms_fwd_x(st))
+            else:
+                lss = [self.steps[i] for i in arg]
+                timed("gemm", 1, sum(2 * ls.M * ls.N * ls.K for ls in lss),
+                      lambda: fp8_linear_gemm_grouped([ls.grad_w_problem() for ls in lss],
+                                                      lss[0].rowwise, st,
+                                                      e5m2=lss[0].e5m2_grad))
+        return groups
 
 
 class PipelinedStep:
@@ -414,8 +522,8 @@ class PipelinedStep:
         self.start.record(self.main)
         self.side.wait_event(self.start)
         for i, ls in enumerate(self.steps):
-            qbytes = 6 * (ls.M * ls.K + ls.N * ls.K + ls.M * ls.N)
-            timed("quantize", 3, qbytes, self.side, lambda: ls.quantize(self.side))
+            timed("quantize", 3 if ls.owns_qx else 2, ls.quantize_bytes, self.side,
+                  lambda: ls.quantize(self.side))
             self.q_done[i].record(self.side)
         for i, ls in enumerate(self.steps):
             self.main.wait_event(self.q_done[i])
@@ -440,7 +548,7 @@ class SwiGLUFFNStep:
       dh = d_out.w2, grad_w2 = d_out^T.h
       da, db and their quantizes                   (fp8_swiglu_bwd)
       grad_x = da.w1, then += db.w3                (fp8_linear_bwd_x_acc)
-      grad_w1 = da^T.x, grad_w3 = db^T.x
+      grad_w1 = da^T.x, grad_w3 = db^T.x           (one grouped launch)
 
     With ``e5m2_grad`` the gradient operands (d_out, da, db) are E5M2.
     """
@@ -538,14 +646,12 @@ class SwiGLUFFNStep:
             ("grad_x_acc", "gemm", g, False, ("qw3",), lambda st: fp8_linear_bwd_x_acc(
                 self.qdb.q, self.qdb.scale, self.qw3.qt, self.qw3.scale_t, M, H, D,
                 self.grad_x, rw, st, e5m2=e5)),
-            ("grad_w1", "gemm", g, False, (), lambda st: fp8_linear_bwd(
-                None, None, self.qda.qt, self.qda.scale_t, None, None, self.qx.qt,
-                self.qx.scale_t, M, H, D, rw, grad_w=self.grad_w1, want_x=False, stream=st,
-                e5m2=e5)),
-            ("grad_w3", "gemm", g, False, (), lambda st: fp8_linear_bwd(
-                None, None, self.qdb.qt, self.qdb.scale_t, None, None, self.qx.qt,
-                self.qx.scale_t, M, H, D, rw, grad_w=self.grad_w3, want_x=False, stream=st,
-                e5m2=e5)),
+            # grad_W of w1 and w3 in one launch: 2 x 896 tiles fill the last
+            # round of 256 compute units that each alone leaves half idle
+            ("grad_w13", "gemm", 2 * g, False, (), lambda st: fp8_linear_gemm_grouped(
+                [(self.qda.qt, self.qda.scale_t, self.qx.qt, self.qx.scale_t, self.grad_w1),
+                 (self.qdb.qt, self.qdb.scale_t, self.qx.qt, self.qx.scale_t, self.grad_w3)],
+                rw, st, e5m2=e5)),
         )
 
     def run(self, side=None, record: bool = False):

@@ -210,6 +210,40 @@ FP8L_API int fp8_linear_bwd_w_f32(const void *dytq, const float *sdyt, const voi
                                   int scaling, float *grad_w, void *stream);
 
 /*
+ * Several independent GEMMs of fp8_linear_fwd's form in one launch:
+ *
+ *   c[i][j] = bf16( fp32( fp32(acc * (1/sa)) * (1/sb) ) ),
+ *   acc     = sum_t value(a[i][t]) * value(b[j][t])        (fp32 accumulate)
+ *
+ * for each problem, a [m, k] (E4M3, or E5M2 with FP8L_E5M2 in scaling),
+ * b [n, k] E4M3, sa / sb tensorwise [1] or rowwise [m] / [n], c [m, n]
+ * bf16 written.  One launch lets a problem whose output tiles leave the
+ * chip's last round partly idle (896 tiles of 256 x 256 on 256 compute
+ * units) share that round with another: e.g. the grad_W of w1 and w3 of
+ * the SwiGLU feed-forward, or any of fp8_linear_bwd's GEMMs.  Each
+ * problem's result is the one its own fp8_linear_fwd-style call gives.
+ *
+ *   problems  host array of count descriptors (read during the call only)
+ *   count     1..FP8L_MAX_GROUP
+ *   scaling   FP8L_TENSORWISE or FP8L_ROWWISE, optionally | FP8L_E5M2,
+ *             for every problem
+ * Dimension, alignment and size rules as for fp8_linear_fwd, per problem;
+ * the outputs must not overlap one another (FP8L_EINVAL).
+ */
+#define FP8L_MAX_GROUP 4
+typedef struct fp8l_gemm_problem {
+    const void *a;
+    const float *sa;
+    const void *b;
+    const float *sb;
+    void *c;
+    int64_t m, n, k;
+} fp8l_gemm_problem;
+
+FP8L_API int fp8_linear_gemm_grouped(const fp8l_gemm_problem *problems, int count, int scaling,
+                                     void *stream);
+
+/*
  * grad_X added into an existing bf16 grad_x: for an x that feeds two linears
  * (w1 and w3 of the SwiGLU feed-forward below), whose gradient is the sum of
  * the two contributions as bf16 tensors add (autograd accumulates the

@@ -245,3 +245,29 @@ def test_swiglu_and_accumulate_entry_points_reject_bad_arguments():
     assert acc(gx=None) == E.FP8L_EINVAL
     assert acc(swt=None) == E.FP8L_EINVAL
     assert acc(gx=A_BAD) == E.FP8L_EALIGN
+
+
+@pytestmark_cpu
+def test_gemm_grouped_rejects_bad_arguments():
+    E = ops
+    L = ops.lib()
+
+    def prob(c=A16, m=16, n=16, k=16, a=A16, sa=A16, b=A16, sb=A16):
+        return ops.GemmProblem(a, sa, b, sb, c, m, n, k)
+
+    def call(probs, count=None, scaling=0):
+        arr = (ops.GemmProblem * max(len(probs), 1))(*probs)
+        return L.fp8_linear_gemm_grouped(arr, len(probs) if count is None else count,
+                                         scaling, None)
+
+    assert L.fp8_linear_gemm_grouped(None, 1, 0, None) == E.FP8L_EINVAL
+    assert call([prob()], count=0) == E.FP8L_EINVAL
+    assert call([prob()] * 5) == E.FP8L_EINVAL                 # more than FP8L_MAX_GROUP
+    assert call([prob()], scaling=4) == E.FP8L_EINVAL
+    assert call([prob(m=24)]) == E.FP8L_ESHAPE
+    assert call([prob(), prob(c=0x20000, k=-16)]) == E.FP8L_ESHAPE
+    assert call([prob(a=None)]) == E.FP8L_EINVAL
+    assert call([prob(sb=None)]) == E.FP8L_EINVAL
+    assert call([prob(c=A_BAD)]) == E.FP8L_EALIGN
+    # outputs overlapping: [A16, A16 + 512) and [A16 + 256, ...)
+    assert call([prob(), prob(c=A16 + 256)]) == E.FP8L_EINVAL

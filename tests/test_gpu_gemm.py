@@ -112,3 +112,39 @@ def test_linear_step_mid_size(rowwise):
     G.gemm_parity(G.host(step.grad_x), gx, ody[0], ow[1], ody[2], ow[3], label="grad_x")
     gw = oracle.gemm_tn(ody[1], ody[3], ox[1], ox[3])
     G.gemm_parity(G.host(step.grad_w), gw, ody[1], ox[1], ody[3], ox[3], label="grad_w")
+
+
+@pytest.mark.parametrize("e5m2", [False, True], ids=["e4m3", "e5m2"])
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+def test_gemm_grouped(rowwise, e5m2):
+    """Up to four GEMMs of different shapes (ragged, one empty, one with a K
+    tail) in one launch: each output equals its own launch bit for bit, and
+    the first is checked against the oracle."""
+    shapes = [(272, 400, 208), (0, 64, 128), (528, 784, 336), (256, 256, 16)]
+    ops_in, outs = [], []
+    for i, (m, n, k) in enumerate(shapes):
+        xa = W.random_bf16(80 + i, (max(m, 16), k), 1e-2 if e5m2 else 1.0, 0)[:m]
+        xb = W.random_bf16(80 + i, (n, k), 0.02, 1)
+        qa = (oracle.quantize_e5m2 if e5m2 else oracle.quantize)(xa, rowwise)
+        qb = oracle.quantize(xb, rowwise)
+        ops_in.append((qa[0], qa[2], qb[0], qb[2]))
+        outs.append(torch.full((m, n), 3.0, dtype=torch.bfloat16, device=G.DEV))
+    dev = [(G.dev_u8(a), G.dev_f32(sa), G.dev_u8(b), G.dev_f32(sb)) for a, sa, b, sb in ops_in]
+    G.say("gemm grouped", shapes, "rowwise", rowwise, "e5m2", e5m2)
+    ops.fp8_linear_gemm_grouped([d + (o,) for d, o in zip(dev, outs)], rowwise, e5m2=e5m2)
+    single = []
+    for (a, sa, b, sb), (m, n, k) in zip(dev, shapes):
+        o = torch.full((m, n), 5.0, dtype=torch.bfloat16, device=G.DEV)
+        ops.fp8_linear_gemm_grouped([(a, sa, b, sb, o)], rowwise, e5m2=e5m2)
+        single.append(o)
+    torch.cuda.synchronize()
+    for i, (g, s) in enumerate(zip(outs, single)):
+        assert torch.equal(g, s), "problem %d differs from its own launch" % i
+    a, sa, b, sb = ops_in[0]
+    want = oracle.gemm_tn_mixed(a, 1 if e5m2 else 0, sa, b, 0, sb)
+    G.gemm_parity(G.host(outs[0]), want, a, b, sa, sb, label="grouped[0]", e5m2_a=e5m2)
+    # a single problem through the group entry equals fp8_linear_fwd
+    if not e5m2:
+        f = ops.fp8_linear_fwd(dev[2][0], dev[2][1], dev[2][2], dev[2][3], rowwise)
+        torch.cuda.synchronize()
+        assert torch.equal(f, single[2])

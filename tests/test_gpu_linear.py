@@ -111,3 +111,32 @@ def test_pipelined_step_equals_serial():
         torch.cuda.synchronize()
         want = [t for r in ref for t in (r.out, r.grad_x, r.grad_w)]
         assert all(torch.equal(p, q) for p, q in zip(g, want))
+
+
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+def test_grouped_step_equals_serial(rowwise):
+    """GroupedStep (X of w1 and w3 quantized once, their grad_W in one
+    grouped launch) gives the outputs of the three LinearSteps run alone."""
+    M, D, H = 528, 272, 784
+    x = G.dev_bf16(W.random_bf16(73, (M, D), 1.0, 0))
+    h = G.dev_bf16(W.random_bf16(73, (M, H), 1.0, 1))
+    ws = [G.dev_bf16(W.random_bf16(73, s, 0.02, 2 + i))
+          for i, s in enumerate(((H, D), (H, D), (D, H)))]
+    dys = [G.dev_bf16(W.random_bf16(73, s, 1e-2, 5 + i))
+           for i, s in enumerate(((M, H), (M, H), (M, D)))]
+    s1 = ops.LinearStep(x, ws[0], dys[0], rowwise)
+    s3 = ops.LinearStep(x, ws[1], dys[1], rowwise, qx=s1.qx)
+    s2 = ops.LinearStep(h, ws[2], dys[2], rowwise)
+    grouped = ops.GroupedStep([s1, s3, s2])
+    assert grouped.plan == [("x", 0), ("x", 1), ("w", [0, 1]), ("x", 2), ("w", [2])]
+    G.say("grouped step", (M, D, H), "rowwise", rowwise)
+    grouped.run()
+    got = [t.clone() for ls in (s1, s3, s2) for t in (ls.out, ls.grad_x, ls.grad_w)]
+    ref = [ops.LinearStep(xx, w, dy, rowwise) for xx, w, dy in
+           ((x, ws[0], dys[0]), (x, ws[1], dys[1]), (h, ws[2], dys[2]))]
+    for r in ref:
+        r.run()
+    torch.cuda.synchronize()
+    want = [t for r in ref for t in (r.out, r.grad_x, r.grad_w)]
+    for i, (p, q) in enumerate(zip(got, want)):
+        assert torch.equal(p, q), "output %d" % i
