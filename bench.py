@@ -131,21 +131,21 @@ def cpu_baseline(wl, rows_g: int, rows_q: int = 512):
 
 
 def measure_e5m2_step(steps, flops_per_step: int, reps: int = 10):
-    """The whole step again with the gradient dY quantized to E5M2 and the
-    backward GEMMs reading it so (same buffers, warmed first); wall time
-    bracketed by device synchronisation, like `value`."""
+    """The whole step again (same launch plan) with the gradient dY quantized
+    to E5M2 and the backward GEMMs reading it so (same buffers, warmed
+    first); wall time bracketed by device synchronisation, like `value`."""
     import torch
+    from float8_mixed_precision_amd import ops
     for ls in steps:
         ls.e5m2_grad = True
     try:
+        grouped = ops.GroupedStep(steps)
         for _ in range(2):
-            for ls in steps:
-                ls.run()
+            grouped.run()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(reps):
-            for ls in steps:
-                ls.run()
+            grouped.run()
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
     finally:

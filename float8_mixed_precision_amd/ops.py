@@ -423,32 +423,49 @@ class LinearStep:
 
 
 class GroupedStep:
-    """The linears of one step on one stream, with the grad_W GEMMs of
-    consecutive linears of the same grad_W shape in one grouped launch (two
-    896-tile grids fill the 256 compute units' last round together instead
-    of each leaving it half idle).  Per linear: its quantizes, the forward
-    GEMM and grad_X; then the grouped grad_W.  Same results as each
+    """The linears of one step on one stream, their GEMMs in few launches.
+
+    Per linear: its quantizes, then one fp8_linear_gemm_grouped launch of
+    its GEMMs (forward, grad_X, grad_W) ordered by contraction length,
+    longest first, so that the short tiles fill in behind the long ones and
+    every compute unit finishes at about the same time.  A grad_W whose
+    shape equals the next linear's is deferred into the next launch (w1's
+    and w3's, 896 tiles each, fill 7 rounds of 256 compute units together).
+    For the Llama FFN that is 3 launches for 9 GEMMs.  Results equal each
     LinearStep's run() in turn.
 
-    ``run(record=True)`` brackets each linear's quantizes, its two GEMMs and
-    each grad_W launch with timing events and returns (kind, launches,
-    work, start, end) per group (kind "quantize" with work in bytes, or
-    "gemm" with work in flops and launches counting kernel dispatches).
+    ``plan`` lists, per linear, the GEMMs of its launch as (kind, linear)
+    with kind "fwd", "grad_x" or "grad_w".  ``run(record=True)`` brackets
+    each linear's quantizes and its GEMM launch with timing events and
+    returns (kind, launches, work, start, end) per group (kind "quantize"
+    with work in bytes, or "gemm" with work in flops).
     """
 
     def __init__(self, steps):
         self.steps = list(steps)
         shape = lambda ls: (ls.N, ls.K, ls.M, ls.rowwise, ls.e5m2_grad)
-        # pairs of consecutive linears with the same grad_W shape
-        self.plan = []          # ("x", i) for fwd + grad_x of i, ("w", [i, ...]) for grad_W
-        i = 0
-        while i < len(self.steps):
-            if i + 1 < len(self.steps) and shape(self.steps[i]) == shape(self.steps[i + 1]):
-                self.plan += [("x", i), ("x", i + 1), ("w", [i, i + 1])]
-                i += 2
+        contraction = {"fwd": lambda ls: ls.K, "grad_x": lambda ls: ls.N,
+                       "grad_w": lambda ls: ls.M}
+        self.plan = []
+        deferred = []
+        for i, ls in enumerate(self.steps):
+            probs = [("fwd", i), ("grad_x", i)]
+            nxt = self.steps[i + 1] if i + 1 < len(self.steps) else None
+            if nxt is not None and not deferred and shape(nxt) == shape(ls):
+                deferred.append(("grad_w", i))
             else:
-                self.plan += [("x", i), ("w", [i])]
-                i += 1
+                probs += deferred + [("grad_w", i)]
+                deferred = []
+            probs.sort(key=lambda p: -contraction[p[0]](self.steps[p[1]]))
+            self.plan.append(probs)
+
+    def _problem(self, kind, i):
+        ls = self.steps[i]
+        if kind == "fwd":
+            return (ls.qx.q, ls.qx.scale, ls.qw.q, ls.qw.scale, ls.out)
+        if kind == "grad_x":
+            return (ls.qdy.q, ls.qdy.scale, ls.qw.qt, ls.qw.scale_t, ls.grad_x)
+        return ls.grad_w_problem()
 
     def run(self, stream=None, record: bool = False):
         st = stream if stream is not None else torch.cuda.current_stream()
@@ -465,18 +482,18 @@ class GroupedStep:
             else:
                 fn()
 
-        for kind, arg in self.plan:
-            if kind == "x":
-                ls = self.steps[arg]
-                timed("quantize", 3 if ls.owns_qx else 2, ls.quantize_bytes,
-                      lambda: ls.quantize(st))
-                timed("gemm", 2, 4 * ls.M * ls.N * ls.K, lambda: ls.gemms_fwd_x(st))
-            else:
-                lss = [self.steps[i] for i in arg]
-                timed("gemm", 1, sum(2 * ls.M * ls.N * ls.K for ls in lss),
-                      lambda: fp8_linear_gemm_grouped([ls.grad_w_problem() for ls in lss],
-                                                      lss[0].rowwise, st,
-                                                      e5m2=lss[0].e5m2_grad))
+        for ls, probs in zip(self.steps, self.plan):
+            timed("quantize", 3 if ls.owns_qx else 2, ls.quantize_bytes,
+                  lambda: ls.quantize(st))
+            flops = sum(2 * self.steps[i].M * self.steps[i].N * self.steps[i].K
+                        for _, i in probs)
+            for c in range(0, len(probs), FP8L_MAX_GROUP):
+                chunk = probs[c:c + FP8L_MAX_GROUP]
+                timed("gemm", 1, flops if len(probs) <= FP8L_MAX_GROUP else
+                      sum(2 * self.steps[i].M * self.steps[i].N * self.steps[i].K
+                          for _, i in chunk),
+                      lambda: fp8_linear_gemm_grouped([self._problem(k, i) for k, i in chunk],
+                                                      ls.rowwise, st, e5m2=ls.e5m2_grad))
         return groups
 
 
@@ -541,14 +558,14 @@ class SwiGLUFFNStep:
     d_out on ``side`` when a second stream is given):
 
       quantize x once (read by w1 and w3), quantize w1, w3, w2
-      a = x.w1^T, b = x.w3^T                       (fp8 GEMMs)
+      a = x.w1^T, b = x.w3^T                       (one grouped launch)
       h = silu(a) * b and its quantize             (fp8_swiglu_fwd)
       out = h.w2^T
       quantize d_out
-      dh = d_out.w2, grad_w2 = d_out^T.h
+      dh = d_out.w2, grad_w2 = d_out^T.h           (one grouped launch)
       da, db and their quantizes                   (fp8_swiglu_bwd)
-      grad_x = da.w1, then += db.w3                (fp8_linear_bwd_x_acc)
-      grad_w1 = da^T.x, grad_w3 = db^T.x           (one grouped launch)
+      grad_x = da.w1, grad_w1 = da^T.x, grad_w3 = db^T.x   (one grouped launch)
+      grad_x += db.w3                              (fp8_linear_bwd_x_acc)
 
     With ``e5m2_grad`` the gradient operands (d_out, da, db) are E5M2.
     """
@@ -615,12 +632,10 @@ class SwiGLUFFNStep:
                                             e5m2=e5)),
             ("qx", "quantize", 6 * M * D, False, (),
              lambda st: fp8_linear_quantize(self.x, rw, self.qx, self.ws, st)),
-            ("a", "gemm", g, False, ("qw1",),
-             lambda st: fp8_linear_fwd(self.qx.q, self.qx.scale, self.qw1.q, self.qw1.scale, rw,
-                                       self.a, st)),
-            ("b", "gemm", g, False, ("qw3",),
-             lambda st: fp8_linear_fwd(self.qx.q, self.qx.scale, self.qw3.q, self.qw3.scale, rw,
-                                       self.b, st)),
+            # a and b in one launch
+            ("ab", "gemm", 2 * g, False, ("qw1", "qw3"), lambda st: fp8_linear_gemm_grouped(
+                [(self.qx.q, self.qx.scale, self.qw1.q, self.qw1.scale, self.a),
+                 (self.qx.q, self.qx.scale, self.qw3.q, self.qw3.scale, self.b)], rw, st)),
             # a, b read twice (elementwise pass, then h read by the cast),
             # h written once; q and qt written
             ("swiglu_fwd", "swiglu", 10 * M * H, False, (),
@@ -628,30 +643,29 @@ class SwiGLUFFNStep:
             ("out", "gemm", g, False, ("qw2",),
              lambda st: fp8_linear_fwd(self.qh.q, self.qh.scale, self.qw2.q, self.qw2.scale, rw,
                                        self.out, st)),
-            ("dh", "gemm", g, False, ("qw2", "qdy"), lambda st: fp8_linear_bwd(
-                self.qdy.q, self.qdy.scale, None, None, self.qw2.qt, self.qw2.scale_t, None,
-                None, M, D, H, rw, grad_x=self.dh, want_w=False, stream=st, e5m2=e5)),
-            ("grad_w2", "gemm", g, False, ("qdy",), lambda st: fp8_linear_bwd(
-                None, None, self.qdy.qt, self.qdy.scale_t, None, None, self.qh.qt,
-                self.qh.scale_t, M, D, H, rw, grad_w=self.grad_w2, want_x=False, stream=st,
-                e5m2=e5)),
+            # grad_W2 (896 tiles, contraction M) and dh (1792 tiles,
+            # contraction D) in one launch, the longer tiles first
+            ("grad_w2_dh", "gemm", 2 * g, False, ("qw2", "qdy"),
+             lambda st: fp8_linear_gemm_grouped(
+                 [(self.qdy.qt, self.qdy.scale_t, self.qh.qt, self.qh.scale_t, self.grad_w2),
+                  (self.qdy.q, self.qdy.scale, self.qw2.qt, self.qw2.scale_t, self.dh)],
+                 rw, st, e5m2=e5)),
             # dh, a, b read; da, db written; each read again by its cast,
             # whose q and qt are written
             ("swiglu_bwd", "swiglu", 18 * M * H, False, (),
              lambda st: fp8_swiglu_bwd(self.dh, self.a, self.b, rw, self.da, self.db, self.qda,
                                        self.qdb, self.ws_sw, st, e5m2=e5)),
-            ("grad_x", "gemm", g, False, ("qw1",), lambda st: fp8_linear_bwd(
-                self.qda.q, self.qda.scale, None, None, self.qw1.qt, self.qw1.scale_t, None,
-                None, M, H, D, rw, grad_x=self.grad_x, want_w=False, stream=st, e5m2=e5)),
+            # grad_x = da.w1 (512 tiles, contraction H) with the grad_W of w1
+            # and w3 (2 x 896 tiles, contraction M) in one launch; then
+            # grad_x += db.w3
+            ("grad_x_w13", "gemm", 3 * g, False, ("qw1",), lambda st: fp8_linear_gemm_grouped(
+                [(self.qda.q, self.qda.scale, self.qw1.qt, self.qw1.scale_t, self.grad_x),
+                 (self.qda.qt, self.qda.scale_t, self.qx.qt, self.qx.scale_t, self.grad_w1),
+                 (self.qdb.qt, self.qdb.scale_t, self.qx.qt, self.qx.scale_t, self.grad_w3)],
+                rw, st, e5m2=e5)),
             ("grad_x_acc", "gemm", g, False, ("qw3",), lambda st: fp8_linear_bwd_x_acc(
                 self.qdb.q, self.qdb.scale, self.qw3.qt, self.qw3.scale_t, M, H, D,
                 self.grad_x, rw, st, e5m2=e5)),
-            # grad_W of w1 and w3 in one launch: 2 x 896 tiles fill the last
-            # round of 256 compute units that each alone leaves half idle
-            ("grad_w13", "gemm", 2 * g, False, (), lambda st: fp8_linear_gemm_grouped(
-                [(self.qda.qt, self.qda.scale_t, self.qx.qt, self.qx.scale_t, self.grad_w1),
-                 (self.qdb.qt, self.qdb.scale_t, self.qx.qt, self.qx.scale_t, self.grad_w3)],
-                rw, st, e5m2=e5)),
         )
 
     def run(self, side=None, record: bool = False):

@@ -115,8 +115,9 @@ def test_pipelined_step_equals_serial():
 
 @pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
 def test_grouped_step_equals_serial(rowwise):
-    """GroupedStep (X of w1 and w3 quantized once, their grad_W in one
-    grouped launch) gives the outputs of the three LinearSteps run alone."""
+    """GroupedStep (X of w1 and w3 quantized once, each linear's GEMMs in one
+    grouped launch, w1's grad_W in w3's) gives the outputs of the three
+    LinearSteps run alone."""
     M, D, H = 528, 272, 784
     x = G.dev_bf16(W.random_bf16(73, (M, D), 1.0, 0))
     h = G.dev_bf16(W.random_bf16(73, (M, H), 1.0, 1))
@@ -128,7 +129,11 @@ def test_grouped_step_equals_serial(rowwise):
     s3 = ops.LinearStep(x, ws[1], dys[1], rowwise, qx=s1.qx)
     s2 = ops.LinearStep(h, ws[2], dys[2], rowwise)
     grouped = ops.GroupedStep([s1, s3, s2])
-    assert grouped.plan == [("x", 0), ("x", 1), ("w", [0, 1]), ("x", 2), ("w", [2])]
+    # w1: grad_x (contraction H) before fwd (D); w3 adds both grad_W
+    # (contraction M); w2: fwd (H), grad_w (M), grad_x (D)
+    assert grouped.plan == [[("grad_x", 0), ("fwd", 0)],
+                            [("grad_x", 1), ("grad_w", 0), ("grad_w", 1), ("fwd", 1)],
+                            [("fwd", 2), ("grad_w", 2), ("grad_x", 2)]]
     G.say("grouped step", (M, D, H), "rowwise", rowwise)
     grouped.run()
     got = [t.clone() for ls in (s1, s3, s2) for t in (ls.out, ls.grad_x, ls.grad_w)]
