@@ -3,17 +3,18 @@
 One step = the whole path for every linear of the workload: quantize X, W
 and dY (amax, scale, saturating E4M3 cast with the transposed copy), the
 forward GEMM and both backward GEMMs, all on device-resident synthetic
-inputs (seeded, Llama-3.1-shaped), on one stream.  The default workload is the Llama-3.1-8B
-SwiGLU FFN (w1 and w3: X[8192x4096].W[14336x4096]^T, w2:
-X[8192x14336].W[4096x14336]^T), tensorwise scaling.
+inputs (seeded, Llama-3.1-shaped), on one stream (ops.GroupedStep: an X read
+by two linears is quantized once, and each linear's GEMMs run as one
+grouped launch).  The default workload is the Llama-3.1-8B SwiGLU FFN (w1
+and w3: X[8192x4096].W[14336x4096]^T, w2: X[8192x14336].W[4096x14336]^T),
+tensorwise scaling.
 
 Prints one JSON line: whole-step TFLOP/s (6*M*N*K per linear), the roofline
 of the dominant kernel (the fp8 GEMM, against the dense fp8 MFMA peak)
-measured with HIP events on the launch stream around each linear's three
-GEMM launches during the timed steps (grouped: an event pair around every
-launch cost about 2% of the step), the
-same for the quantize chain against HBM bandwidth, and the CPU oracle timed
-on a bounded sample on the host cores.
+measured with HIP events on the launch stream around each GEMM launch and
+each linear's group of quantizes during the timed steps, the same for the
+quantize chain against HBM bandwidth, and the CPU oracle timed on a bounded
+sample on the host cores.
 """
 from __future__ import annotations
 
@@ -395,8 +396,8 @@ def main():
                    "flops_per_step": wl.flops},
         "pct_fp8_peak_step": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "roofline": {
-            "kernel": "k_gemm_fp8_tn (fwd, grad_x, grad_w; the grad_w of w1 and w3 in one "
-                      "grouped launch)",
+            "kernel": "k_gemm_fp8_tn (each linear's fwd, grad_x and grad_w in one grouped "
+                      "launch; w1's grad_w in w3's)",
             "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
             "traffic": traffic,
