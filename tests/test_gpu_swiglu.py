@@ -83,14 +83,30 @@ def test_swiglu_fwd(shape, rowwise):
 
 
 def test_swiglu_fwd_every_bf16_gate():
-    """a takes every bf16 pattern (NaNs, infinities, subnormals included)
-    against b = 1 and against random b."""
+    """a takes every bf16 pattern (NaNs, infinities, subnormals included, and
+    both sides of the range whose silu values come from the table) against
+    b = 1 and against random b."""
     a = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(4096, 16)
     for name, b in (("b=1", np.full(a.shape, 0x3F80, np.uint16)),
                     ("b random", W.random_bf16(61, a.shape, 1.0, 0))):
         G.say("swiglu fwd every gate", name)
         h, _ = _run_fwd(a, b, False)
         assert_bf16_equal(h, oracle.swiglu_fwd(a, b), name)
+
+
+@pytest.mark.parametrize("rowwise", [False, True], ids=RW_IDS)
+def test_swiglu_bwd_every_bf16_gate(rowwise):
+    """da and db with a taking every bf16 pattern (both sides of the range
+    whose silu values come from the table, zeros, subnormals, infinities,
+    NaN), random b and dh."""
+    a = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(4096, 16)
+    b = W.random_bf16(68, a.shape, 1.0, 0)
+    dh = W.random_bf16(68, a.shape, 1e-2, 1)
+    G.say("swiglu bwd every gate", "rowwise", rowwise)
+    da, db, _, _ = _run_bwd(dh, a, b, rowwise, False)
+    wda, wdb = oracle.swiglu_bwd(dh, a, b)
+    assert_bf16_equal(da, wda, "da every gate")
+    assert_bf16_equal(db, wdb, "db every gate")
 
 
 @pytest.mark.parametrize("rowwise", [False, True], ids=RW_IDS)
