@@ -301,6 +301,59 @@ def measure_next_rows(steps, stream, reps: int = 5):
     return out
 
 
+def measure_board(run_step, seconds: float = 2.5):
+    """Engine clock and board power while the step runs back to back for
+    `seconds` (the driver's averaged readings through torch.cuda /
+    amdsmi, sampled every 50 ms over the second half of the run, when the
+    readings reflect the load), and the same readings at idle beforehand.
+    Returns None where the readings are unavailable."""
+    import threading
+    import torch
+    try:
+        torch.cuda.clock_rate(0)
+        torch.cuda.power_draw(0)
+    except Exception:
+        return None
+    samples, phase, stop = [], ["idle"], [False]
+
+    def sampler():
+        while not stop[0]:
+            try:
+                samples.append((phase[0], time.perf_counter(), float(torch.cuda.clock_rate(0)),
+                                float(torch.cuda.power_draw(0))))
+            except Exception:
+                pass
+            time.sleep(0.05)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(0.6)
+    phase[0] = "load"
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            run_step()
+            n += 1
+        torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stop[0] = True
+    th.join()
+    load = [s for s in samples if s[0] == "load" and s[1] >= t0 + (t1 - t0) / 2]
+    idle = [s for s in samples if s[0] == "idle"]
+    if not load:
+        return None
+    mean = lambda xs: round(sum(xs) / len(xs), 1)
+    return {"clock_mhz": mean([s[2] for s in load]),
+            "power_w": mean([s[3] for s in load]),
+            "power_w_max": max(s[3] for s in load),
+            "idle_clock_mhz": mean([s[2] for s in idle]) if idle else None,
+            "idle_power_w": mean([s[3] for s in idle]) if idle else None,
+            "samples": len(load), "steps": n, "seconds": round(t1 - t0, 2),
+            "source": "torch.cuda.clock_rate / power_draw (amdsmi averages) while the step "
+                      "runs back to back"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -427,6 +480,11 @@ def main():
             result["next_rows"]["ffn_block"] = blk
             result["next_rows"]["ffn_block_e5m2"] = measure_ffn_block(steps, wl, stream,
                                                                       e5m2_grad=True)
+    if not args.no_next_rows:
+        # last of the GPU measurements: 2.5 s of back-to-back steps heat the
+        # chip, which would bias whatever is timed after it
+        print("[bench] board clock and power", file=sys.stderr, flush=True)
+        result["board"] = measure_board(lambda: run_step(False))
     del steps, shared, grouped
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -358,9 +358,12 @@ AmaxGeom amax_geom(int64_t rows, int64_t cols) {
   return {cdiv(rows, AM_TR), cdiv(cols, AM_TC)};
 }
 
+// As many workgroups as keep every one at the same number of chunks (the
+// grid-stride loop then ends in one round), at most TW_MAX_BLOCKS.
 int64_t tw_blocks(int64_t rows, int64_t cols) {
   const int64_t nchunks = cdiv(rows * cols / 8, TW_CHUNK);
-  return nchunks < TW_MAX_BLOCKS ? nchunks : TW_MAX_BLOCKS;
+  if (nchunks <= TW_MAX_BLOCKS) return nchunks;
+  return cdiv(nchunks, cdiv(nchunks, TW_MAX_BLOCKS));
 }
 
 }  // namespace
