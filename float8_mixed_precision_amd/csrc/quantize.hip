@@ -180,26 +180,55 @@ __global__ __launch_bounds__(AM_THREADS) void k_amax_partial(
 
 // ------------------------------------------------------------- finalize --
 
-// one thread per output: rows first (max over tiles_c partials), then columns
+// One scale per row and per column from the partial maxima.  Workgroups
+// [0, nbr) cover 64 rows each (max over tiles_c row partials), the rest 64
+// columns each (max over tiles_r column partials).  Thread (o, sl), o =
+// tid % 64, sl = tid / 64, reduces partials sl, sl + 4, ... of output o with
+// eight loads in flight at a time (index clamped into the array, value
+// masked), and the four slices meet in LDS.  (One thread per output walking
+// its partials serially took as long as the amax pass itself.)
+constexpr int FR_OUT = 64;
+constexpr int FR_SLICES = 4;
+constexpr int FR_UNROLL = 8;
 template <int FMT>
 __global__ __launch_bounds__(256) void k_finalize_rowwise(
     const uint16_t *__restrict__ rowpart, const uint16_t *__restrict__ colpart,
-    int rows, int cols, int tiles_c, int tiles_r, float *scale, float *scale_t,
+    int rows, int cols, int tiles_c, int tiles_r, int nbr, float *scale, float *scale_t,
     float *amax_out) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < rows) {
-    uint32_t m = 0;
-    for (int t = 0; t < tiles_c; ++t) m = max(m, (uint32_t)rowpart[(size_t)t * rows + i]);
+  const int o = threadIdx.x % FR_OUT;
+  const int sl = threadIdx.x / FR_OUT;
+  const bool is_row = (int)blockIdx.x < nbr;
+  const int n = is_row ? rows : cols;                 // >= 1 for any launched block
+  const int T = is_row ? tiles_c : tiles_r;
+  const uint16_t *__restrict__ part = is_row ? rowpart : colpart;
+  const int i = (is_row ? (int)blockIdx.x : (int)blockIdx.x - nbr) * FR_OUT + o;
+  const int ic = i < n ? i : n - 1;
+  uint32_t m = 0;
+  for (int t0 = sl; t0 < T; t0 += FR_SLICES * FR_UNROLL) {
+    uint32_t v[FR_UNROLL];
+#pragma unroll
+    for (int u = 0; u < FR_UNROLL; ++u) {
+      const int t = t0 + FR_SLICES * u;
+      v[u] = part[(size_t)(t < T ? t : T - 1) * n + ic];
+    }
+#pragma unroll
+    for (int u = 0; u < FR_UNROLL; ++u)
+      if (t0 + FR_SLICES * u < T) m = max(m, v[u]);
+  }
+  __shared__ uint32_t red[FR_SLICES][FR_OUT];
+  red[sl][o] = m;
+  __syncthreads();
+  if (sl == 0 && i < n) {
+#pragma unroll
+    for (int k = 1; k < FR_SLICES; ++k) m = max(m, red[k][o]);
     const float a = bf16_to_f32(m);
-    scale[i] = scale_from_amax<FMT>(a);
-    if (amax_out) amax_out[i] = a;
-  } else if (i < rows + cols) {
-    const int c = i - rows;
-    uint32_t m = 0;
-    for (int t = 0; t < tiles_r; ++t) m = max(m, (uint32_t)colpart[(size_t)t * cols + c]);
-    const float a = bf16_to_f32(m);
-    scale_t[c] = scale_from_amax<FMT>(a);
-    if (amax_out) amax_out[rows + c] = a;
+    if (is_row) {
+      scale[i] = scale_from_amax<FMT>(a);
+      if (amax_out) amax_out[i] = a;
+    } else {
+      scale_t[i] = scale_from_amax<FMT>(a);
+      if (amax_out) amax_out[rows + i] = a;
+    }
   }
 }
 
@@ -391,10 +420,11 @@ hipError_t finish_fmt(const void *x, int64_t rows, int64_t cols, bool rowwise, i
     const AmaxGeom g = amax_geom(rows, cols);
     uint16_t *rowpart, *colpart;
     quantize_rowwise_partials(workspace, rows, cols, &rowpart, &colpart);
-    if (rows + cols > 0)
-      hipLaunchKernelGGL(k_finalize_rowwise<FMT>, dim3((unsigned)cdiv(rows + cols, 256)),
-                         dim3(256), 0, stream, rowpart, colpart, R, C, (int)g.tiles_c,
-                         (int)g.tiles_r, scale, scale_t, amax_out);
+    const int64_t nbr = cdiv(rows, FR_OUT), nbc = cdiv(cols, FR_OUT);
+    if (nbr + nbc > 0)
+      hipLaunchKernelGGL(k_finalize_rowwise<FMT>, dim3((unsigned)(nbr + nbc)), dim3(256), 0,
+                         stream, rowpart, colpart, R, C, (int)g.tiles_c, (int)g.tiles_r,
+                         (int)nbr, scale, scale_t, amax_out);
   } else if (nparts == 0) {
     hipLaunchKernelGGL(k_finalize_tw_empty<FMT>, dim3(1), dim3(64), 0, stream, scale,
                        scale_t, amax_out);
