@@ -301,6 +301,59 @@ def measure_next_rows(steps, stream, reps: int = 5):
     return out
 
 
+def measure_workload_step(name: str, reps: int = 20, warmup: int = 3):
+    """The whole step of another workload (its own seeded tensors, freed
+    afterwards), timed like `value`, with the GEMM and quantize-chain
+    rooflines from the same kind of HIP events."""
+    import torch
+    from float8_mixed_precision_amd import ops
+    from float8_mixed_precision_amd import workloads as W
+
+    wl = W.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    data = W.generate(wl)
+    steps, shared, qx_of = [], {}, {}
+    for lin, d in zip(wl.linears, data):
+        key = id(d["x"])
+        if key not in shared:
+            shared[key] = W.bits_to_torch(d["x"], dev)
+        steps.append(ops.LinearStep(shared[key], W.bits_to_torch(d["w"], dev),
+                                    W.bits_to_torch(d["dy"], dev), wl.rowwise,
+                                    qx=qx_of.get(key)))
+        qx_of.setdefault(key, steps[-1].qx)
+    del data
+    grouped = ops.GroupedStep(steps)
+    for _ in range(warmup):
+        grouped.run()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        evs += grouped.run(record=True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    g_fl = sum(w for k, _, w, _, _ in evs if k == "gemm")
+    g_ms = sum(a.elapsed_time(b) for k, _, _, a, b in evs if k == "gemm")
+    q_b = sum(w for k, _, w, _, _ in evs if k == "quantize")
+    q_ms = sum(a.elapsed_time(b) for k, _, _, a, b in evs if k == "quantize")
+    gt = g_fl / (g_ms * 1e-3) / 1e12
+    qg = q_b / (q_ms * 1e-3) / 1e9
+    out = {"workload": wl.name, "description": wl.description,
+           "scaling": "rowwise" if wl.rowwise else "tensorwise",
+           "value": round(wl.flops * reps / el / 1e12, 2), "unit": "TFLOP/s",
+           "steps": reps, "ms_per_step": round(el * 1e3 / reps, 4),
+           "gemm": {"bound": "mfma", "achieved": round(gt, 2), "peak": PEAK_FP8_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(gt / PEAK_FP8_TFLOPS, 4)},
+           "quantize": {"bound": "hbm", "achieved": round(qg, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(qg / PEAK_HBM_GBS, 4),
+                        "bytes_per_element": 6},
+           "time_split_ms_per_step": {"gemm": round(g_ms / reps, 4),
+                                      "quantize": round(q_ms / reps, 4)}}
+    del steps, shared, grouped, evs
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_board(run_step, seconds: float = 2.5):
     """Engine clock and board power while the step runs back to back for
     `seconds` (the driver's averaged readings through torch.cuda /
@@ -480,6 +533,10 @@ def main():
             result["next_rows"]["ffn_block"] = blk
             result["next_rows"]["ffn_block_e5m2"] = measure_ffn_block(steps, wl, stream,
                                                                       e5m2_grad=True)
+    if not args.no_next_rows and args.workload == "ffn8b_tw":
+        # its own tensors next to the FFN's (a few GB of 288)
+        print("[bench] rowwise outlier step", file=sys.stderr, flush=True)
+        result["next_rows"]["rowwise_step"] = measure_workload_step("outlier_rw")
     if not args.no_next_rows:
         # last of the GPU measurements: 2.5 s of back-to-back steps heat the
         # chip, which would bias whatever is timed after it
