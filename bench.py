@@ -537,6 +537,10 @@ def main():
         # its own tensors next to the FFN's (a few GB of 288)
         print("[bench] rowwise outlier step", file=sys.stderr, flush=True)
         result["next_rows"]["rowwise_step"] = measure_workload_step("outlier_rw")
+        print("[bench] 8B attention projection and 70B-shaped FFN steps", file=sys.stderr,
+              flush=True)
+        result["next_rows"]["attn8b_step"] = measure_workload_step("attn8b_tw")
+        result["next_rows"]["ffn70b_step"] = measure_workload_step("ffn70b_tw", reps=10)
     if not args.no_next_rows:
         # last of the GPU measurements: 2.5 s of back-to-back steps heat the
         # chip, which would bias whatever is timed after it
