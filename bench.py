@@ -39,7 +39,7 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="ffn8b_tw")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timing (e.g. under a profiler)")
@@ -301,10 +301,14 @@ def measure_next_rows(steps, stream, reps: int = 5):
     return out
 
 
-def measure_workload_step(name: str, reps: int = 20, warmup: int = 3):
+def measure_workload_step(name: str, reps: int = 20, warmup_s: float = 0.3,
+                          min_timed_s: float = 0.1):
     """The whole step of another workload (its own seeded tensors, freed
     afterwards), timed like `value`, with the GEMM and quantize-chain
-    rooflines from the same kind of HIP events."""
+    rooflines from the same kind of HIP events.  The warm-up runs for
+    warmup_s seconds (the tensors are generated on the host first, and the
+    GPU comes out of that idle at a low clock), and at least min_timed_s
+    seconds of steps are timed."""
     import torch
     from float8_mixed_precision_amd import ops
     from float8_mixed_precision_amd import workloads as W
@@ -323,9 +327,15 @@ def measure_workload_step(name: str, reps: int = 20, warmup: int = 3):
         qx_of.setdefault(key, steps[-1].qx)
     del data
     grouped = ops.GroupedStep(steps)
-    for _ in range(warmup):
-        grouped.run()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < warmup_s:
+        for _ in range(4):
+            grouped.run()
+        torch.cuda.synchronize()
+        n += 4
+    per_step = (time.perf_counter() - t0) / n
+    reps = max(reps, int(min_timed_s / per_step) + 1)
     evs = []
     t0 = time.perf_counter()
     for _ in range(reps):
