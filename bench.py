@@ -364,6 +364,52 @@ def measure_workload_step(name: str, reps: int = 20, warmup_s: float = 0.3,
     return out
 
 
+def measure_mfma_ceiling(codes, stream, target_ms: float = 25.0, launches: int = 4):
+    """The fp8 MFMA instruction alone (libfp8probe's k_mfma_loop: register
+    operands, the GEMM's 8 x 8 accumulator layout and snake order, no
+    memory traffic) on one workgroup per compute unit, timed with HIP events
+    over `launches` launches of about target_ms each: on the step's own
+    E4M3 codes, and on all-zero codes (the least switching).  The first is
+    the rate the GEMM's main loop could reach on this data under the board's
+    power limit."""
+    import ctypes
+    import torch
+    from float8_mixed_precision_amd import build as B
+
+    L = ctypes.CDLL(B.PROBE_PATH)
+    P, i64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.fp8_probe_mfma_loop.restype = I
+    L.fp8_probe_mfma_loop.argtypes = [P, i64, I, I, P, P]
+    wg, per_wg = 256, 4 * 512 * 2 * 16 * 16 * 128      # flops per workgroup per iteration
+    sink = torch.empty(wg * 256, dtype=torch.float32, device=codes.device)
+    zeros = torch.zeros(1 << 20, dtype=torch.uint8, device=codes.device)
+    hs = ctypes.c_void_p(stream.cuda_stream)
+
+    def run(buf, iters, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            if L.fp8_probe_mfma_loop(buf.data_ptr(), buf.numel(), wg, iters,
+                                     sink.data_ptr(), hs) != 0:
+                raise RuntimeError("fp8_probe_mfma_loop failed")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    ms = run(codes, 200, 1)
+    iters = max(200, int(200 * target_ms / max(ms, 1e-3)))
+    out = {"kernel": "k_mfma_loop: v_mfma_f32_16x16x128_f8f6f4 on register operands, "
+                     "one 256-thread workgroup per compute unit", "unit": "TFLOP/s",
+           "peak": PEAK_FP8_TFLOPS, "iters": iters, "launches": launches}
+    for name, buf in (("e4m3_codes", codes), ("zero_codes", zeros)):
+        run(buf, iters, 1)
+        t = run(buf, iters, launches)
+        v = wg * per_wg * iters * launches / (t * 1e-3) / 1e12
+        out[name] = {"achieved": round(v, 1), "frac": round(v / PEAK_FP8_TFLOPS, 4)}
+    return out
+
+
 def measure_board(run_step, seconds: float = 2.5):
     """Engine clock and board power while the step runs back to back for
     `seconds` (the driver's averaged readings through torch.cuda /
@@ -532,6 +578,11 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_next_rows:
+        print("[bench] MFMA-only ceiling", file=sys.stderr, flush=True)
+        ceil = measure_mfma_ceiling(steps[0].qx.q, stream)
+        ceil["gemm_fraction_of_e4m3_ceiling"] = round(gemm_tflops / ceil["e4m3_codes"]["achieved"], 4)
+        ceil["codes"] = "the step's E4M3 codes of X (N(0,1) activations scaled onto 448)"
+        result["mfma_ceiling"] = ceil
         print("[bench] next rows", file=sys.stderr, flush=True)
         result["next_rows"] = measure_next_rows(steps, stream)
         result["next_rows"]["e5m2_grad_step"] = measure_e5m2_step(steps, wl.flops)

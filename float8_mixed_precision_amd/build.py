@@ -10,6 +10,10 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libfp8linear.so")
 SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "swiglu.hip"]
+# measurement support, kept out of the method's library: the MFMA-only
+# throughput probe that bench.py reports beside the GEMM's roofline
+PROBE_SOURCES = ["mfma_probe.hip"]
+PROBE_PATH = os.path.join(LIB_DIR, "libfp8probe.so")
 ARCH = os.environ.get("FP8L_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -22,16 +26,21 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into one shared library (always rebuilds)."""
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = ["hipcc"] + HIPCC_FLAGS + srcs + ["-o", tmp]
+def _hipcc(sources, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["hipcc"] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (every HIP source of the method) and the MFMA
+    probe library; always rebuilds."""
+    os.makedirs(LIB_DIR, exist_ok=True)
+    _hipcc(SOURCES, LIB_PATH, verbose)
+    _hipcc(PROBE_SOURCES, PROBE_PATH, verbose)
     return LIB_PATH
 
 

@@ -271,3 +271,22 @@ def test_gemm_grouped_rejects_bad_arguments():
     assert call([prob(c=A_BAD)]) == E.FP8L_EALIGN
     # outputs overlapping: [A16, A16 + 512) and [A16 + 256, ...)
     assert call([prob(), prob(c=A16 + 256)]) == E.FP8L_EINVAL
+
+
+@pytestmark_cpu
+def test_mfma_probe_library_rejects_bad_arguments():
+    """The measurement-only MFMA probe (bench.py's mfma_ceiling) loads and
+    validates its arguments before launching anything."""
+    import ctypes
+    from float8_mixed_precision_amd import build as B
+    L = ctypes.CDLL(B.PROBE_PATH)
+    P, i64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    f = L.fp8_probe_mfma_loop
+    f.restype = I
+    f.argtypes = [P, i64, I, I, P, P]
+    assert f(None, 1 << 20, 1, 1, A16, None) == 1
+    assert f(A16, 1 << 20, 1, 1, None, None) == 1
+    assert f(A16, 1 << 14, 1, 1, A16, None) == 1          # below one 32 KB slice
+    assert f(A16, 1 << 20, 0, 1, A16, None) == 1
+    assert f(A16, 1 << 20, 1, 0, A16, None) == 1
+    assert f(A16 + 16, 1 << 20, 1, 1, A16, None) == 1     # codes not 32-byte aligned
