@@ -516,15 +516,25 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(GemmGroup g) {
     }
     return;
   }
+  // rowwise: the lane's reciprocal scales, read from LDS once here (the
+  // staging stores below write LDS too, so reads inside that loop would be
+  // repeated for every block)
+  float inv_ar[NF];
+  v4f inv_br[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    inv_ar[f] = RW ? inv[wm * WM + f * FR + (lane_e & 15)] : inv_a0;
+    inv_br[f] = (v4f){inv_b0, inv_b0, inv_b0, inv_b0};
+    if (RW) inv_br[f] = *reinterpret_cast<const v4f *>(inv + BM + wn * WN + f * FR + nq);
+  }
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
     const int ml = i * FR + (lane_e & 15);              // row within the wave tile
-    const float inv_a = RW ? inv[wm * WM + ml] : inv_a0;
+    const float inv_a = inv_ar[i];
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
       const int nl = j * FR + nq;                       // col within the wave tile
-      v4f ib = {inv_b0, inv_b0, inv_b0, inv_b0};
-      if (RW) ib = *reinterpret_cast<const v4f *>(inv + BM + wn * WN + nl);
+      const v4f ib = inv_br[j];
       f32x2 v01 = {(acc[j][i][0] * inv_a) * ib[0], (acc[j][i][1] * inv_a) * ib[1]};
       f32x2 v23 = {(acc[j][i][2] * inv_a) * ib[2], (acc[j][i][3] * inv_a) * ib[3]};
       const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
