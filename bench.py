@@ -414,7 +414,7 @@ def measure_board(run_step, seconds: float = 2.5):
     """Engine clock and board power while the step runs back to back for
     `seconds` (the driver's averaged readings through torch.cuda /
     amdsmi, sampled every 50 ms over the second half of the run, when the
-    readings reflect the load), and the same readings at idle beforehand.
+    readings reflect the load; they lag the load by a few hundred ms).
     Returns None where the readings are unavailable."""
     import threading
     import torch
@@ -436,7 +436,6 @@ def measure_board(run_step, seconds: float = 2.5):
 
     th = threading.Thread(target=sampler, daemon=True)
     th.start()
-    time.sleep(0.6)
     phase[0] = "load"
     t0 = time.perf_counter()
     n = 0
@@ -449,15 +448,12 @@ def measure_board(run_step, seconds: float = 2.5):
     stop[0] = True
     th.join()
     load = [s for s in samples if s[0] == "load" and s[1] >= t0 + (t1 - t0) / 2]
-    idle = [s for s in samples if s[0] == "idle"]
     if not load:
         return None
     mean = lambda xs: round(sum(xs) / len(xs), 1)
     return {"clock_mhz": mean([s[2] for s in load]),
             "power_w": mean([s[3] for s in load]),
             "power_w_max": max(s[3] for s in load),
-            "idle_clock_mhz": mean([s[2] for s in idle]) if idle else None,
-            "idle_power_w": mean([s[3] for s in idle]) if idle else None,
             "samples": len(load), "steps": n, "seconds": round(t1 - t0, 2),
             "source": "torch.cuda.clock_rate / power_draw (amdsmi averages) while the step "
                       "runs back to back"}

@@ -190,6 +190,7 @@ __global__ __launch_bounds__(AM_THREADS) void k_amax_partial(
 constexpr int FR_OUT = 64;
 constexpr int FR_SLICES = 4;
 constexpr int FR_UNROLL = 8;
+static_assert(FR_OUT * FR_SLICES == 256, "one finalize workgroup is 256 threads");
 template <int FMT>
 __global__ __launch_bounds__(256) void k_finalize_rowwise(
     const uint16_t *__restrict__ rowpart, const uint16_t *__restrict__ colpart,
