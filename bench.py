@@ -74,15 +74,17 @@ def gemm_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """HBM bytes per GEMM launch from committed rocprofv3 counter runs, valid
-    only while the GEMM source is the one the counters were taken on."""
+    only for the workload and the GEMM source the counters were taken on."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    if t.get("workload", "").split(" ")[0] != workload:
         return None
     return t.get("bytes_per_launch")
 
@@ -533,7 +535,7 @@ def main():
     quant_gbs = q_bytes / (q_ms * 1e-3) / 1e9
     value = wl.flops * args.steps / elapsed / 1e12
 
-    traffic = measured_traffic()
+    traffic = measured_traffic(wl.name)
     result = {
         "metric": "fp8 linear fwd+bwd TFLOP/s at Llama-3.1-8B FFN shape; % fp8 MFMA peak",
         "value": round(value, 2),
