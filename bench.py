@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--ffn-block-only", action="store_true",
                    help="only measure the SwiGLU FFN block (profiling runs of its kernels); "
                         "prints its JSON object and exits")
+    p.add_argument("--phase-timing", action="store_true",
+                   help="only time the GEMM's phases per workgroup (the measurement build "
+                        "libfp8phase.so) at the 8B FFN GEMM shapes and exit")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="only run 3 plain device copies of this many bytes (the "
                         "calibration kernel for HBM byte counters) and exit")
@@ -461,6 +464,70 @@ def measure_board(run_step, seconds: float = 2.5):
                       "runs back to back"}
 
 
+def phase_timing():
+    """Per-workgroup phases of the GEMM (libfp8phase.so: the same kernels
+    with shader-clock and 100 MHz real-time counters read at a workgroup's
+    start, after its prologue, after its main loop and after its last store)
+    for the forward, grad_X and grad_W shapes of the 8B FFN's w1, each
+    launched back to back on E4M3 codes of N(0,1) activations and N(0,0.02)
+    weights quantized by this library.  Medians over the workgroups of the
+    last launch; the clock is shader cycles over real time."""
+    import ctypes
+    import numpy as np
+    import torch
+    from float8_mixed_precision_amd import build as B
+    from float8_mixed_precision_amd import ops
+
+    ops.LIB_PATH = B.PHASE_PATH
+    L = ops.lib()
+    L.fp8_gemm_phase_read.restype = ctypes.c_int
+    L.fp8_gemm_phase_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    out = []
+    for name, (M, N, K) in (("fwd", (8192, 14336, 4096)), ("grad_x", (8192, 4096, 14336)),
+                            ("grad_w", (14336, 4096, 8192))):
+        a = (torch.randn(M, K, device=dev, generator=gen)).to(torch.bfloat16)
+        b = (torch.randn(N, K, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+        qa, qb = ops.fp8_linear_quantize(a), ops.fp8_linear_quantize(b)
+        o = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        launch = lambda: ops.fp8_linear_gemm_grouped([(qa.q, qa.scale, qb.q, qb.scale, o)])
+        for _ in range(30):
+            launch()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 20 * 1e3
+        nb = (M // 256) * (N // 256)
+        buf = np.zeros(nb * 8, dtype=np.uint64)
+        if L.fp8_gemm_phase_read(buf.ctypes.data, buf.nbytes) != 0:
+            raise RuntimeError("fp8_gemm_phase_read failed")
+        d = buf.reshape(nb, 8).astype(np.int64)
+        t0, r0, ta, ra, t1, r1, t2, r2 = (d[:, i] for i in range(8))
+        nk = K // 128
+        clk = (t2 - t0) / ((r2 - r0) / 100e6) / 1e9
+        loop = float(np.median(t1 - ta))
+        tile = float(np.median(t2 - t0))
+        out.append({"gemm": name, "M_N_K": [M, N, K], "workgroups": nb,
+                    "avg_launch_us": round(us, 1),
+                    "tflops": round(2 * M * N * K / us / 1e6, 1),
+                    "clock_ghz_median": round(float(np.median(clk)), 3),
+                    "clock_ghz_min_max": [round(float(clk.min()), 3), round(float(clk.max()), 3)],
+                    "prologue_cycles": int(np.median(ta - t0)),
+                    "loop_cycles_per_ktile": round(loop / nk, 1),
+                    "loop_issue_efficiency": round(2048 * nk / loop, 4),
+                    "epilogue_cycles": int(np.median(t2 - t1)),
+                    "tile_cycles": int(tile),
+                    "mfma_share_of_tile": round(2048 * nk / tile, 4)})
+        del a, b, qa, qb, o
+    print(json.dumps({"phase_timing": out}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -469,6 +536,9 @@ def main():
         sys.exit(2)
     if args.copy_bytes:
         copy_calibration(args.copy_bytes)
+        return
+    if args.phase_timing:
+        phase_timing()
         return
 
     import numpy as np

@@ -14,6 +14,10 @@ SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "swiglu.hip"]
 # throughput probe that bench.py reports beside the GEMM's roofline
 PROBE_SOURCES = ["mfma_probe.hip"]
 PROBE_PATH = os.path.join(LIB_DIR, "libfp8probe.so")
+# measurement support: the library again, with per-workgroup phase
+# timestamps in the GEMM (bench.py --phase-timing)
+PHASE_PATH = os.path.join(LIB_DIR, "libfp8phase.so")
+PHASE_FLAGS = ["-DFP8L_PHASE_TIMING"]
 ARCH = os.environ.get("FP8L_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -26,21 +30,24 @@ HIPCC_FLAGS = [
 ]
 
 
-def _hipcc(sources, out: str, verbose: bool) -> None:
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["hipcc"] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, out)
-
-
 def build(verbose: bool = False) -> str:
-    """Compile the library (every HIP source of the method) and the MFMA
-    probe library; always rebuilds."""
+    """Compile the library (every HIP source of the method) and the two
+    measurement libraries, in parallel; always rebuilds."""
     os.makedirs(LIB_DIR, exist_ok=True)
-    _hipcc(SOURCES, LIB_PATH, verbose)
-    _hipcc(PROBE_SOURCES, PROBE_PATH, verbose)
+    jobs = []
+    for sources, out, extra in ((SOURCES, LIB_PATH, []), (PROBE_SOURCES, PROBE_PATH, []),
+                                (SOURCES, PHASE_PATH, PHASE_FLAGS)):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = (["hipcc"] + HIPCC_FLAGS + extra + [os.path.join(CSRC, s) for s in sources] +
+               ["-o", tmp])
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((subprocess.Popen(cmd), cmd, tmp, out))
+    failed = [cmd for p, cmd, _, _ in jobs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
+    for _, _, tmp, out in jobs:
+        os.replace(tmp, out)
     return LIB_PATH
 
 

@@ -72,6 +72,16 @@
 #include "fp8l_internal.h"
 
 namespace fp8l {
+#ifdef FP8L_PHASE_TIMING
+// Measurement build only (a separate library compiled with
+// -DFP8L_PHASE_TIMING): per workgroup, the shader-clock counter (s_memtime)
+// and the 100 MHz real-time counter (s_memrealtime) at the kernel's start,
+// after the prologue, after the main loop and after the last store is
+// issued, written by thread 0 for the first PHASE_MAX_BLOCKS workgroups of
+// the latest launch.  Read with fp8_gemm_phase_read.
+constexpr int PHASE_MAX_BLOCKS = 8192;
+__device__ unsigned long long g_phase[PHASE_MAX_BLOCKS * 8];
+#endif
 namespace {
 
 constexpr int BM = 256;
@@ -221,6 +231,11 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(GemmGroup g) {
                 tni);
   const int m0 = tmi * BM;
   const int n0 = tni * BN;
+#ifdef FP8L_PHASE_TIMING
+  const unsigned long long ph_t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long ph_r0 = __builtin_amdgcn_s_memrealtime();
+  unsigned long long ph_ta = ph_t0, ph_ra = ph_r0;
+#endif
 
   // rowwise: the tile's 256 + 256 reciprocal scales, one of each per thread,
   // into their own LDS region (read after the main loop's last barrier)
@@ -422,6 +437,10 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(GemmGroup g) {
     for (int f = 0; f < 4; ++f) { FP8L_RD(0, 0, f, 0); FP8L_RD(0, 0, f, 1); }
 #pragma unroll
     for (int f = 0; f < 7; ++f) { FP8L_RD(0, 1, f, 0); FP8L_RD(0, 1, f, 1); }
+#ifdef FP8L_PHASE_TIMING
+    ph_ta = __builtin_amdgcn_s_memtime();
+    ph_ra = __builtin_amdgcn_s_memrealtime();
+#endif
     int t = 0;
     // k-tiles with a DMA of k-tile t+2 into the stage just drained
     for (; t + 2 < nk; ++t) {
@@ -452,6 +471,10 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(GemmGroup g) {
 #undef FP8L_RD
 #undef FP8L_DMA1
 
+#ifdef FP8L_PHASE_TIMING
+  const unsigned long long ph_t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long ph_r1 = __builtin_amdgcn_s_memrealtime();
+#endif
   // ---- epilogue, staged through LDS: after one barrier every wave is done
   // with the operand stages; each wave writes its scaled bf16 128 x 128 tile
   // to its own region (rows padded to 272 bytes), then stores whole rows
@@ -584,6 +607,15 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(GemmGroup g) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off[u], 0, C_STORE_AUX);
   }
+#ifdef FP8L_PHASE_TIMING
+  if (tid == 0 && blockIdx.x < PHASE_MAX_BLOCKS) {
+    const unsigned long long ph_t2 = __builtin_amdgcn_s_memtime();
+    const unsigned long long ph_r2 = __builtin_amdgcn_s_memrealtime();
+    unsigned long long *d = g_phase + (size_t)blockIdx.x * 8;
+    d[0] = ph_t0; d[1] = ph_r0; d[2] = ph_ta; d[3] = ph_ra;
+    d[4] = ph_t1; d[5] = ph_r1; d[6] = ph_t2; d[7] = ph_r2;
+  }
+#endif
 }
 
 }  // namespace
@@ -662,3 +694,15 @@ hipError_t gemm_f32_launch(const uint8_t *A, const float *sa, const uint8_t *B,
 }
 
 }  // namespace fp8l
+
+#ifdef FP8L_PHASE_TIMING
+// Copies the first `bytes` of the timestamp array (8 u64 per workgroup:
+// memtime, realtime at start, after the prologue, after the main loop, at
+// the end) to host memory; synchronous.  Returns 0, or 5 on a HIP error.
+extern "C" __attribute__((visibility("default"))) int fp8_gemm_phase_read(void *host,
+                                                                          size_t bytes) {
+  if (bytes > sizeof(fp8l::g_phase)) bytes = sizeof(fp8l::g_phase);
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(fp8l::g_phase), bytes, 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? 0 : 5;
+}
+#endif
