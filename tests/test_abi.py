@@ -120,6 +120,15 @@ def test_gemm_entry_points_reject_bad_arguments():
     assert fwd(wq=A_BAD) == E.FP8L_EALIGN
     assert fwd(out=A_BAD) == E.FP8L_EALIGN
     assert fwd(sx=A16 + 1) == E.FP8L_EALIGN
+    # operands and outputs are addressed with 32-bit byte offsets: a matrix
+    # of 2^31 bytes is rejected, one row less gets past the size check (and
+    # stops at the misaligned output, before any launch)
+    assert fwd(M=32768, N=32768, K=16) == E.FP8L_ESHAPE          # bf16 out: 2^31 B
+    assert fwd(M=32752, N=32768, K=16, out=A_BAD) == E.FP8L_EALIGN
+    assert fwd(M=65536, N=16, K=32768) == E.FP8L_ESHAPE          # xq: 2^31 B
+    assert fwd(M=65520, N=16, K=32768, out=A_BAD) == E.FP8L_EALIGN
+    assert fwd(M=16, N=65536, K=32768) == E.FP8L_ESHAPE          # wq: 2^31 B
+    assert fwd(M=1 << 31, N=16, K=16) == E.FP8L_ESHAPE           # dimension cap
 
     def bwd(gx=A16, gw=A16, dyq=A16, wtq=A_BAD, **kw):
         return L.fp8_linear_bwd(P(dyq) if dyq else None, P(A16), P(A16), P(A16),
@@ -134,6 +143,8 @@ def test_gemm_entry_points_reject_bad_arguments():
     assert bwd(wtq=None) == E.FP8L_EINVAL
     assert bwd(gw=A_BAD, wtq=A16) == E.FP8L_EALIGN   # grad_w output checked
     assert bwd(scaling=4) == E.FP8L_EINVAL
+    assert bwd(M=32768, N=16, K=32768) == E.FP8L_ESHAPE     # grad_x bf16 [M, K]: 2^31 B
+    assert bwd(M=65536, N=32768, K=16) == E.FP8L_ESHAPE     # dyq [M, N]: 2^31 B
 
 
 @pytestmark_cpu
