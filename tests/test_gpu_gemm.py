@@ -148,3 +148,54 @@ def test_gemm_grouped(rowwise, e5m2):
         f = ops.fp8_linear_fwd(dev[2][0], dev[2][1], dev[2][2], dev[2][3], rowwise)
         torch.cuda.synchronize()
         assert torch.equal(f, single[2])
+
+
+def _sampled_parity_at(a, sa, b, sb, out, rows, cols, label):
+    """The oracle's values at rows x cols (every pair) against out's."""
+    ii, jj = (np.repeat(rows, len(cols)), np.tile(cols, len(rows)))
+    want = oracle.gemm_tn_sampled(a, sa, b, sb, ii, jj)
+    got = G.host(out[torch.as_tensor(ii, device=G.DEV), torch.as_tensor(jj, device=G.DEV)])
+    G.gemm_parity(got, want, a, b, sa, sb, ii=ii, jj=jj, label=label)
+
+
+def test_gemm_output_at_the_offset_limit():
+    """The largest accepted bf16 output: [32752, 32768] is 2^31 - 2^20 bytes,
+    so the kernel's 32-bit store offsets reach their largest values.  The
+    first and last rows and columns and a random sample match the oracle,
+    and a guard region right after the output stays untouched."""
+    M, N, K = 32752, 32768, 256
+    rng = np.random.default_rng(93)
+    import tests.pins as pins
+    a, b = pins.random_codes(rng, (M, K)), pins.random_codes(rng, (N, K))
+    sa, sb = np.float32(3.5), np.float32(0.75)
+    guard = 1 << 16
+    buf = torch.full((M * N + guard,), -7.0, dtype=torch.bfloat16, device=G.DEV)
+    out = buf[:M * N].view(M, N)
+    G.say("gemm at the output offset limit", (M, N, K))
+    ops.fp8_linear_fwd(G.dev_u8(a), G.dev_f32(sa), G.dev_u8(b), G.dev_f32(sb), False, out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.all(buf[M * N:] == -7.0)), "write past the output"
+    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], rng.integers(0, M, 24)]))
+    cols = np.unique(np.concatenate([[0, 1, N - 2, N - 1], rng.integers(0, N, 24)]))
+    _sampled_parity_at(a, sa, b, sb, out, rows, cols, "output offset limit")
+
+
+def test_gemm_operand_at_the_offset_limit():
+    """The largest accepted fp8 operand: A [65520, 32768] is 2^31 - 2^19
+    bytes, so the kernel's 32-bit load offsets reach their largest values
+    (N = 16: one partial tile column)."""
+    M, N, K = 65520, 16, 32768
+    rng = np.random.default_rng(94)
+
+    def codes(shape):          # random finite E4M3 codes, generated as bytes
+        c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        c[(c & 0x7F) == 0x7F] ^= 1
+        return c
+
+    a, b = codes((M, K)), codes((N, K))
+    sa, sb = np.float32(1.25), np.float32(2.0)
+    G.say("gemm at the operand offset limit", (M, N, K))
+    out = ops.fp8_linear_fwd(G.dev_u8(a), G.dev_f32(sa), G.dev_u8(b), G.dev_f32(sb), False)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], rng.integers(0, M, 60)]))
+    _sampled_parity_at(a, sa, b, sb, out, rows, np.arange(N), "operand offset limit")
