@@ -183,3 +183,38 @@ def test_quantize_scaled_max_maps_to_448():
     q, qt, s, st, am = G.gpu_quantize(x, True)
     assert np.all((q[np.abs(f) == np.abs(f).max(axis=1, keepdims=True)] & 0x7F) == 0x7E)
     assert np.all((qt.T[np.abs(f) == np.abs(f).max(axis=0, keepdims=True)] & 0x7F) == 0x7E)
+
+
+def test_quantize_beyond_2_31_elements():
+    """A tensorwise quantize of bf16 [65536, 32768] (2^31 elements, 4 GiB):
+    element offsets pass 2^31, so the 64-bit indexing of the amax pass and
+    of the cast is exercised.  The scale matches the oracle's scale of the
+    host amax bit for bit; sampled rows of q and of qT (first, last and
+    random) match the oracle's cast of those elements with that scale."""
+    R, C, B = 65536, 32768, 4096
+    rng = np.random.default_rng(95)
+    # bf16 patterns with random sign and mantissa, exponents 2^-7 .. 2^0: a
+    # random [4096, C] block repeated down the rows (row r holds block row
+    # r % 4096), so the host side stays cheap at this size
+    blk = rng.integers(0, 1 << 16, size=(B, C), dtype=np.uint16)
+    blk = (blk & 0x807F) | ((120 + ((blk >> 7) & 7)) << 7).astype(np.uint16)
+    x = np.tile(blk, (R // B, 1))
+    amax_bits = int((blk & 0x7FFF).max())
+    want_scale = oracle.scale_from_amax(np.float32(oracle.bf16_to_f32(np.uint16(amax_bits))))
+    G.say("quantize beyond 2^31 elements", (R, C))
+    xd = G.dev_bf16(x)
+    qz = ops.fp8_linear_quantize(xd, False)
+    torch.cuda.synchronize()
+    del xd
+    got_scale = G.host(qz.scale)
+    assert got_scale.view(np.uint32)[0] == np.float32(want_scale).view(np.uint32), \
+        (got_scale[0], want_scale)
+    s = np.float32(want_scale)
+    rows = np.unique(np.concatenate([[0, R - 2, R - 1], rng.integers(0, R, 13)]))
+    q_rows = G.host(qz.q[torch.as_tensor(rows, device=G.DEV)])
+    want_q = oracle.quantize_scaled(blk[rows % B], s)[0]
+    assert np.array_equal(q_rows, want_q), "q rows differ"
+    cols = np.unique(np.concatenate([[0, C - 2, C - 1], rng.integers(0, C, 13)]))
+    qt_rows = G.host(qz.qt[torch.as_tensor(cols, device=G.DEV)])
+    want_qt = oracle.quantize_scaled(np.ascontiguousarray(np.tile(blk[:, cols].T, (1, R // B))), s)[0]
+    assert np.array_equal(qt_rows, want_qt), "qT rows differ"
