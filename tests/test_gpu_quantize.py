@@ -200,7 +200,8 @@ def test_quantize_beyond_2_31_elements():
     blk = (blk & 0x807F) | ((120 + ((blk >> 7) & 7)) << 7).astype(np.uint16)
     x = np.tile(blk, (R // B, 1))
     amax_bits = int((blk & 0x7FFF).max())
-    want_scale = oracle.scale_from_amax(np.float32(oracle.bf16_to_f32(np.uint16(amax_bits))))
+    amax = np.float32(np.asarray(oracle.bf16_to_f32(np.array([amax_bits], np.uint16))).ravel()[0])
+    want_scale = oracle.scale_from_amax(amax)
     G.say("quantize beyond 2^31 elements", (R, C))
     xd = G.dev_bf16(x)
     qz = ops.fp8_linear_quantize(xd, False)
