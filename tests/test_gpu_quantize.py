@@ -185,12 +185,16 @@ def test_quantize_scaled_max_maps_to_448():
     assert np.all((qt.T[np.abs(f) == np.abs(f).max(axis=0, keepdims=True)] & 0x7F) == 0x7E)
 
 
-def test_quantize_beyond_2_31_elements():
-    """A tensorwise quantize of bf16 [65536, 32768] (2^31 elements, 4 GiB):
-    element offsets pass 2^31, so the 64-bit indexing of the amax pass and
-    of the cast is exercised.  The scale matches the oracle's scale of the
-    host amax bit for bit; sampled rows of q and of qT (first, last and
-    random) match the oracle's cast of those elements with that scale."""
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+def test_quantize_beyond_2_31_elements(rowwise):
+    """A quantize of bf16 [65536, 32768] (2^31 elements, 4 GiB): element
+    offsets pass 2^31, so the 64-bit indexing of the amax passes, the
+    rowwise finalize and the cast is exercised.  Sampled rows of q and of
+    qT (first, last and random) and their scales match the oracle bit for
+    bit.  Tensorwise: the oracle's scale of the host amax and its cast of
+    those elements with that scale.  Rowwise: a row's q and row scale are
+    the oracle's rowwise quantize of that row alone, and a column's qT and
+    column scale that of the column alone."""
     R, C, B = 65536, 32768, 4096
     rng = np.random.default_rng(95)
     # bf16 patterns with random sign and mantissa, exponents 2^-7 .. 2^0: a
@@ -199,23 +203,32 @@ def test_quantize_beyond_2_31_elements():
     blk = rng.integers(0, 1 << 16, size=(B, C), dtype=np.uint16)
     blk = (blk & 0x807F) | ((120 + ((blk >> 7) & 7)) << 7).astype(np.uint16)
     x = np.tile(blk, (R // B, 1))
-    amax_bits = int((blk & 0x7FFF).max())
-    amax = np.float32(np.asarray(oracle.bf16_to_f32(np.array([amax_bits], np.uint16))).ravel()[0])
-    want_scale = oracle.scale_from_amax(amax)
-    G.say("quantize beyond 2^31 elements", (R, C))
+    G.say("quantize beyond 2^31 elements", (R, C), "rowwise", rowwise)
     xd = G.dev_bf16(x)
-    qz = ops.fp8_linear_quantize(xd, False)
+    qz = ops.fp8_linear_quantize(xd, rowwise)
     torch.cuda.synchronize()
     del xd
-    got_scale = G.host(qz.scale)
-    assert got_scale.view(np.uint32)[0] == np.float32(want_scale).view(np.uint32), \
-        (got_scale[0], want_scale)
-    s = np.float32(want_scale)
     rows = np.unique(np.concatenate([[0, R - 2, R - 1], rng.integers(0, R, 13)]))
-    q_rows = G.host(qz.q[torch.as_tensor(rows, device=G.DEV)])
-    want_q = oracle.quantize_scaled(blk[rows % B], s)[0]
-    assert np.array_equal(q_rows, want_q), "q rows differ"
     cols = np.unique(np.concatenate([[0, C - 2, C - 1], rng.integers(0, C, 13)]))
+    q_rows = G.host(qz.q[torch.as_tensor(rows, device=G.DEV)])
     qt_rows = G.host(qz.qt[torch.as_tensor(cols, device=G.DEV)])
-    want_qt = oracle.quantize_scaled(np.ascontiguousarray(np.tile(blk[:, cols].T, (1, R // B))), s)[0]
-    assert np.array_equal(qt_rows, want_qt), "qT rows differ"
+    f32 = lambda v: np.asarray(v, np.float32).view(np.uint32)
+    if not rowwise:
+        amax_bits = int((blk & 0x7FFF).max())
+        amax = np.float32(np.asarray(oracle.bf16_to_f32(np.array([amax_bits], np.uint16))).ravel()[0])
+        s = np.float32(oracle.scale_from_amax(amax))
+        assert f32(G.host(qz.scale))[0] == f32(s), (G.host(qz.scale)[0], s)
+        assert np.array_equal(q_rows, oracle.quantize_scaled(blk[rows % B], s)[0]), "q rows"
+        col_bits = np.ascontiguousarray(np.tile(blk[:, cols].T, (1, R // B)))
+        assert np.array_equal(qt_rows, oracle.quantize_scaled(col_bits, s)[0]), "qT rows"
+        return
+    scale, scale_t = G.host(qz.scale), G.host(qz.scale_t)
+    for i, r in enumerate(rows):
+        q1, _, s1, _, _ = oracle.quantize(blk[[r % B]], True)
+        assert np.array_equal(q_rows[i], q1[0]), "q row %d" % r
+        assert f32(scale[r]) == f32(s1[0]), ("row scale", r)
+    for i, c in enumerate(cols):
+        col = np.ascontiguousarray(np.tile(blk[:, c], R // B).reshape(R, 1))
+        _, qt1, _, st1, _ = oracle.quantize(col, True)
+        assert np.array_equal(qt_rows[i], qt1[0]), "qT row %d" % c
+        assert f32(scale_t[c]) == f32(st1[0]), ("column scale", c)
