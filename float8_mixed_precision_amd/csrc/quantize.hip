@@ -274,11 +274,23 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
   const bool col_ok = c < cols;
   constexpr bool ROWWISE = MODE == MODE_RW;
 
+  // rowwise scale vectors 16-byte aligned (the interface promises 4): read
+  // them as float4, else one float at a time
+  const bool vec_scales =
+      ROWWISE && ((reinterpret_cast<uintptr_t>(scale) | reinterpret_cast<uintptr_t>(scale_t)) &
+                  15u) == 0;
   float sc[8];                    // column scales (rowwise) of the 8 columns
   float s_t = 0.f;                // tensor scale
   if (ROWWISE) {
+    if (col_ok && vec_scales) {
+      const float4 a = *reinterpret_cast<const float4 *>(scale_t + c);
+      const float4 b = *reinterpret_cast<const float4 *>(scale_t + c + 4);
+      sc[0] = a.x; sc[1] = a.y; sc[2] = a.z; sc[3] = a.w;
+      sc[4] = b.x; sc[5] = b.y; sc[6] = b.z; sc[7] = b.w;
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sc[j] = col_ok ? scale_t[c + j] : 0.f;
+      for (int j = 0; j < 8; ++j) sc[j] = col_ok ? scale_t[c + j] : 0.f;
+    }
   } else if (MODE == MODE_GIVEN) {
     s_t = scale[0];
   } else {
@@ -301,6 +313,17 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
     const bool ok = col_ok && r < rows;
     uint32_t lo[4], hi[4];               // qt codes: cols 0-3 / 4-7 of each row
     if (ok) {
+      // the 4 rows' scales (rowwise; r is a multiple of 4)
+      float srs[4] = {s_t, s_t, s_t, s_t};
+      if (ROWWISE) {
+        if (vec_scales) {
+          const float4 v = *reinterpret_cast<const float4 *>(scale + r);
+          srs[0] = v.x; srs[1] = v.y; srs[2] = v.z; srs[3] = v.w;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) srs[j] = scale[r + j];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const U4 v = load16(x + (size_t)(r + j) * cols + c);
@@ -309,7 +332,7 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
         f[2] = bf16_to_f32(v.y & 0xFFFFu); f[3] = bf16_to_f32(v.y >> 16);
         f[4] = bf16_to_f32(v.z & 0xFFFFu); f[5] = bf16_to_f32(v.z >> 16);
         f[6] = bf16_to_f32(v.w & 0xFFFFu); f[7] = bf16_to_f32(v.w >> 16);
-        const float s = ROWWISE ? scale[r + j] : s_t;
+        const float s = srs[j];
         const uint32_t q0 = fp8x4<FMT>(f[0] * s, f[1] * s, f[2] * s, f[3] * s);
         const uint32_t q1 = fp8x4<FMT>(f[4] * s, f[5] * s, f[6] * s, f[7] * s);
         *reinterpret_cast<uint2 *>(q + (size_t)(r + j) * cols + c) = make_uint2(q0, q1);

@@ -89,6 +89,27 @@ def test_quantize_shapes(shape, rowwise):
                                 "%s %s" % (shape, name))
 
 
+
+@pytest.mark.parametrize("offset", [0, 1, 2, 3], ids=lambda o: "scale+%dB" % (4 * o))
+def test_quantize_rowwise_scale_alignment(offset):
+    """Rowwise scale vectors at every 4-byte alignment (the interface requires
+    4; 16-byte aligned ones are read as float4, the others one by one): the
+    same bytes and scales as the oracle."""
+    rows, cols = 272, 400
+    x = W.random_bf16(5, (rows, cols), 1.0, 0)
+    sbuf = torch.zeros(rows + 8, dtype=torch.float32, device=G.DEV)
+    stbuf = torch.zeros(cols + 8, dtype=torch.float32, device=G.DEV)
+    qz = ops.Quantized(torch.empty((rows, cols), dtype=torch.uint8, device=G.DEV),
+                       torch.empty((cols, rows), dtype=torch.uint8, device=G.DEV),
+                       sbuf[offset:offset + rows], stbuf[offset:offset + cols],
+                       torch.empty(rows + cols, dtype=torch.float32, device=G.DEV))
+    G.say("quantize rowwise, scale vectors offset by", 4 * offset, "bytes")
+    ops.fp8_linear_quantize(G.dev_bf16(x), True, out=qz)
+    torch.cuda.synchronize()
+    got = (G.host(qz.q), G.host(qz.qt), G.host(qz.scale), G.host(qz.scale_t), G.host(qz.amax))
+    G.assert_quantize_equal(got, oracle.quantize(x, True), "scale offset %d" % offset)
+
+
 @pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
 def test_quantize_special_tensors(rowwise):
     shape = (272, 400)
