@@ -305,7 +305,19 @@ def measure_next_rows(steps, stream, reps: int = 5):
         if r == 0:
             torch.cuda.synchronize()
             rec["cast_hbm"].clear()
+    # reference for cast_hbm: a plain device copy of 1 GiB (torch's copy
+    # kernel; as many bytes read as written), the practical HBM rate for a
+    # stream that reads and writes in equal parts
+    rec["copy_reference"] = []
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=steps[0].x.device)
+    dst = torch.empty_like(src)
+    for r in range(reps + 1):
+        timed("copy_reference", 2 * src.numel(), lambda: dst.copy_(src))
+        if r == 0:
+            torch.cuda.synchronize()
+            rec["copy_reference"].clear()
     torch.cuda.synchronize()
+    del src, dst
     out = {}
     for kind, v in rec.items():
         work = sum(w for w, _, _ in v)
@@ -319,7 +331,7 @@ def measure_next_rows(steps, stream, reps: int = 5):
             ach = work / (ms * 1e-3) / 1e9
             out[kind] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                         "bytes_per_element": 2 if kind == "amax" else 4,
+                         "bytes_per_element": {"amax": 2, "copy_reference": 2}.get(kind, 4),
                          "calls": len(v), "avg_call_us": round(ms * 1e3 / len(v), 2)}
     return out
 
