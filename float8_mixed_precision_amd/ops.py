@@ -431,8 +431,11 @@ class GroupedStep:
     every compute unit finishes at about the same time.  A grad_W whose
     shape equals the next linear's is deferred into the next launch (w1's
     and w3's, 896 tiles each, fill 7 rounds of 256 compute units together).
-    For the Llama FFN that is 3 launches for 9 GEMMs.  Results equal each
-    LinearStep's run() in turn.
+    For the Llama FFN that is 3 launches for 9 GEMMs.  A launch reads
+    every problem's A operand in one code format, so with E5M2 gradients
+    the forward GEMM (E4M3 X) gets a launch of its own, apart from the
+    GEMMs that read dY (``launches()``).  Results equal each LinearStep's
+    run() in turn.
 
     ``plan`` lists, per linear, the GEMMs of its launch as (kind, linear)
     with kind "fwd", "grad_x" or "grad_w".  ``run(record=True)`` brackets
@@ -485,16 +488,31 @@ class GroupedStep:
         for ls, probs in zip(self.steps, self.plan):
             timed("quantize", 3 if ls.owns_qx else 2, ls.quantize_bytes,
                   lambda: ls.quantize(st))
-            flops = sum(2 * self.steps[i].M * self.steps[i].N * self.steps[i].K
-                        for _, i in probs)
-            for c in range(0, len(probs), FP8L_MAX_GROUP):
-                chunk = probs[c:c + FP8L_MAX_GROUP]
-                timed("gemm", 1, flops if len(probs) <= FP8L_MAX_GROUP else
-                      sum(2 * self.steps[i].M * self.steps[i].N * self.steps[i].K
-                          for _, i in chunk),
+            for e5, chunk in self.launches(probs):
+                flops = sum(2 * self.steps[i].M * self.steps[i].N * self.steps[i].K
+                            for _, i in chunk)
+                timed("gemm", 1, flops,
                       lambda: fp8_linear_gemm_grouped([self._problem(k, i) for k, i in chunk],
-                                                      ls.rowwise, st, e5m2=ls.e5m2_grad))
+                                                      ls.rowwise, st, e5m2=e5))
         return groups
+
+    def a_is_e5m2(self, kind, i) -> bool:
+        """Whether problem (kind, i) reads its A operand as E5M2: the
+        backward GEMMs read dY's copies, which are E5M2 under e5m2_grad;
+        the forward GEMM reads X's, always E4M3."""
+        return kind != "fwd" and self.steps[i].e5m2_grad
+
+    def launches(self, probs):
+        """The fp8_linear_gemm_grouped launches of one linear's problems:
+        (e5m2, chunk) pairs.  The code format of A is one per launch, so
+        problems are split by it (in the order of first appearance, each
+        part keeping the longest-contraction-first order), and each part
+        into chunks of at most FP8L_MAX_GROUP."""
+        parts = {}
+        for p in probs:
+            parts.setdefault(self.a_is_e5m2(*p), []).append(p)
+        return [(e5, part[c:c + FP8L_MAX_GROUP]) for e5, part in parts.items()
+                for c in range(0, len(part), FP8L_MAX_GROUP)]
 
 
 class PipelinedStep:

@@ -113,11 +113,13 @@ def test_pipelined_step_equals_serial():
         assert all(torch.equal(p, q) for p, q in zip(g, want))
 
 
+@pytest.mark.parametrize("e5m2", [False, True], ids=["e4m3_grad", "e5m2_grad"])
 @pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
-def test_grouped_step_equals_serial(rowwise):
+def test_grouped_step_equals_serial(rowwise, e5m2):
     """GroupedStep (X of w1 and w3 quantized once, each linear's GEMMs in one
     grouped launch, w1's grad_W in w3's) gives the outputs of the three
-    LinearSteps run alone."""
+    LinearSteps run alone; with E5M2 gradients too, where the forward GEMM
+    (E4M3 X) must not be read in the gradients' format."""
     M, D, H = 528, 272, 784
     x = G.dev_bf16(W.random_bf16(73, (M, D), 1.0, 0))
     h = G.dev_bf16(W.random_bf16(73, (M, H), 1.0, 1))
@@ -125,19 +127,19 @@ def test_grouped_step_equals_serial(rowwise):
           for i, s in enumerate(((H, D), (H, D), (D, H)))]
     dys = [G.dev_bf16(W.random_bf16(73, s, 1e-2, 5 + i))
            for i, s in enumerate(((M, H), (M, H), (M, D)))]
-    s1 = ops.LinearStep(x, ws[0], dys[0], rowwise)
-    s3 = ops.LinearStep(x, ws[1], dys[1], rowwise, qx=s1.qx)
-    s2 = ops.LinearStep(h, ws[2], dys[2], rowwise)
+    s1 = ops.LinearStep(x, ws[0], dys[0], rowwise, e5m2_grad=e5m2)
+    s3 = ops.LinearStep(x, ws[1], dys[1], rowwise, e5m2_grad=e5m2, qx=s1.qx)
+    s2 = ops.LinearStep(h, ws[2], dys[2], rowwise, e5m2_grad=e5m2)
     grouped = ops.GroupedStep([s1, s3, s2])
     # w1: grad_x (contraction H) before fwd (D); w3 adds both grad_W
     # (contraction M); w2: fwd (H), grad_w (M), grad_x (D)
     assert grouped.plan == [[("grad_x", 0), ("fwd", 0)],
                             [("grad_x", 1), ("grad_w", 0), ("grad_w", 1), ("fwd", 1)],
                             [("fwd", 2), ("grad_w", 2), ("grad_x", 2)]]
-    G.say("grouped step", (M, D, H), "rowwise", rowwise)
+    G.say("grouped step", (M, D, H), "rowwise", rowwise, "e5m2", e5m2)
     grouped.run()
     got = [t.clone() for ls in (s1, s3, s2) for t in (ls.out, ls.grad_x, ls.grad_w)]
-    ref = [ops.LinearStep(xx, w, dy, rowwise) for xx, w, dy in
+    ref = [ops.LinearStep(xx, w, dy, rowwise, e5m2_grad=e5m2) for xx, w, dy in
            ((x, ws[0], dys[0]), (x, ws[1], dys[1]), (h, ws[2], dys[2]))]
     for r in ref:
         r.run()
