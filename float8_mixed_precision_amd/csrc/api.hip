@@ -1,7 +1,12 @@
 // C ABI of the Float8 linear library (declared in include/fp8_linear.h):
 // argument validation on the host, then asynchronous launches on the
-// caller's stream.  Nothing here allocates, synchronizes or keeps state.
+// caller's stream.  Nothing here allocates or synchronizes; the only state
+// is the per-device address of the no-allocation entry point's scratch
+// array, looked up once per device.
 #include "fp8l_internal.h"
+
+#include <atomic>
+#include <mutex>
 
 namespace {
 
@@ -37,6 +42,68 @@ int check_gemm_operands(const void *a, const float *sa, const void *b,
   return FP8L_OK;
 }
 
+// ---- scratch of fp8_linear_quantize_noalloc -------------------------------
+// One array per GPU, held until the process ends; every noalloc call on a
+// GPU uses that GPU's copy.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): it passes the
+// device address that hipGetSymbolAddress returns for the device, taken
+// once per device with that device current and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[FP8L_NOALLOC_MAX_WORKSPACE];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch address on the device of `stream` (the current device for the
+// default stream); FP8L_EHIP if it cannot be found.
+int scratch_address(hipStream_t stream, void **out) {
+  int dev = -1;
+  if (stream) {
+    hipDevice_t d;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return FP8L_EHIP;
+    dev = (int)d;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return FP8L_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return FP8L_EHIP;
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = -1;
+      if (hipGetDevice(&cur) != hipSuccess) return FP8L_EHIP;
+      if (cur != dev && hipSetDevice(dev) != hipSuccess) return FP8L_EHIP;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev && hipSetDevice(cur) != hipSuccess) return FP8L_EHIP;
+      if (e != hipSuccess || !p) return FP8L_EHIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FP8L_OK;
+}
+
+// Argument checks shared by the quantize entry points (everything but the
+// workspace); FP8L_OK if the call is valid.
+int check_quantize_args(const void *x, int64_t rows, int64_t cols, int scaling, const void *q,
+                        const void *qt, const float *scale, const float *scale_t,
+                        const float *amax_out) {
+  if (bad_scaling(scaling)) return FP8L_EINVAL;
+  if (bad_dim(rows) || bad_dim(cols) || rows * cols > kMaxElems) return FP8L_ESHAPE;
+  const bool empty = rows == 0 || cols == 0;
+  // scale vectors may be NULL only where they have no entries (rowwise, 0 rows
+  // or 0 columns); tensorwise scales always have one entry
+  const bool rw = (scaling & FP8L_ROWWISE) != 0;
+  if ((!scale && (!rw || rows > 0)) || (!scale_t && (!rw || cols > 0))) return FP8L_EINVAL;
+  if (!empty && (!x || !q || !qt)) return FP8L_EINVAL;
+  if (misaligned(x) || misaligned(q) || misaligned(qt)) return FP8L_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(scale) & 3u) || (reinterpret_cast<uintptr_t>(scale_t) & 3u) ||
+      (reinterpret_cast<uintptr_t>(amax_out) & 3u))
+    return FP8L_EALIGN;
+  return FP8L_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -51,25 +118,34 @@ int fp8_linear_quantize(const void *x, int64_t rows, int64_t cols, int scaling,
                         void *q, void *qt, float *scale, float *scale_t,
                         float *amax_out, void *workspace, size_t workspace_bytes,
                         void *stream) {
-  if (bad_scaling(scaling)) return FP8L_EINVAL;
-  if (bad_dim(rows) || bad_dim(cols) || rows * cols > kMaxElems) return FP8L_ESHAPE;
-  const bool empty = rows == 0 || cols == 0;
-  // scale vectors may be NULL only where they have no entries (rowwise, 0 rows
-  // or 0 columns); tensorwise scales always have one entry
-  const bool rw = (scaling & FP8L_ROWWISE) != 0;
-  if ((!scale && (!rw || rows > 0)) || (!scale_t && (!rw || cols > 0))) return FP8L_EINVAL;
-  if (!empty && (!x || !q || !qt)) return FP8L_EINVAL;
+  const int s = check_quantize_args(x, rows, cols, scaling, q, qt, scale, scale_t, amax_out);
+  if (s != FP8L_OK) return s;
   const size_t need = fp8l::quantize_workspace_bytes(rows, cols, scaling);
   if (need > 0 && !workspace) return FP8L_EINVAL;
   if (workspace_bytes < need) return FP8L_EWORKSPACE;
-  if (misaligned(x) || misaligned(q) || misaligned(qt) || misaligned(workspace))
-    return FP8L_EALIGN;
-  if ((reinterpret_cast<uintptr_t>(scale) & 3u) || (reinterpret_cast<uintptr_t>(scale_t) & 3u) ||
-      (reinterpret_cast<uintptr_t>(amax_out) & 3u))
-    return FP8L_EALIGN;
+  if (misaligned(workspace)) return FP8L_EALIGN;
   hipError_t e = fp8l::quantize_launch(x, rows, cols, scaling, q, qt, scale, scale_t,
                                        amax_out, workspace,
                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
+}
+
+int fp8_linear_quantize_noalloc(const void *x, int64_t rows, int64_t cols, int scaling,
+                                void *q, void *qt, float *scale, float *scale_t,
+                                float *amax_out, void *stream) {
+  const int s = check_quantize_args(x, rows, cols, scaling, q, qt, scale, scale_t, amax_out);
+  if (s != FP8L_OK) return s;
+  // checked before any HIP call: an oversized request fails on the host
+  if (fp8l::quantize_workspace_bytes(rows, cols, scaling) > FP8L_NOALLOC_MAX_WORKSPACE)
+    return FP8L_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void *ws = nullptr;
+  const int sa = scratch_address(st, &ws);
+  if (sa != FP8L_OK) return sa;
+  // every partial maximum the cast reads is written by this call's amax
+  // pass first, so the array needs no clearing between calls
+  hipError_t e = fp8l::quantize_launch(x, rows, cols, scaling, q, qt, scale, scale_t, amax_out,
+                                       ws, st);
   return e == hipSuccess ? FP8L_OK : FP8L_EHIP;
 }
 

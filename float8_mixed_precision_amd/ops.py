@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(HERE, "_lib", "libfp8linear.so")
 
 FP8L_OK, FP8L_EINVAL, FP8L_ESHAPE, FP8L_EALIGN, FP8L_EWORKSPACE, FP8L_EHIP = range(6)
 FP8L_TENSORWISE, FP8L_ROWWISE, FP8L_E5M2 = 0, 1, 2
-EXPORTS = ("fp8_linear_workspace_bytes", "fp8_linear_quantize", "fp8_linear_amax",
+EXPORTS = ("fp8_linear_workspace_bytes", "fp8_linear_quantize",
+           "fp8_linear_quantize_noalloc", "fp8_linear_amax",
            "fp8_linear_quantize_scaled", "fp8_linear_fwd", "fp8_linear_bwd",
            "fp8_linear_bwd_w_f32", "fp8_linear_bwd_x_acc", "fp8_linear_gemm_grouped",
            "fp8_linear_encode_e4m3",
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.fp8_linear_workspace_bytes.argtypes = [i64, i64, I]
     L.fp8_linear_quantize.restype = I
     L.fp8_linear_quantize.argtypes = [P, i64, i64, I, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.fp8_linear_quantize_noalloc.restype = I
+    L.fp8_linear_quantize_noalloc.argtypes = [P, i64, i64, I, P, P, P, P, P, P]
     L.fp8_linear_fwd.restype = I
     L.fp8_linear_fwd.argtypes = [P, P, P, P, i64, i64, i64, I, P, P]
     L.fp8_linear_bwd.restype = I
@@ -164,6 +167,25 @@ def fp8_linear_quantize(x: torch.Tensor, rowwise: bool = False,
         _p(x), rows, cols, _scaling(rowwise, e5m2), _p(out.q), _p(out.qt), _p(out.scale),
         _p(out.scale_t), _p(out.amax), _p(workspace), workspace.numel(), _stream(stream)),
         "fp8_linear_quantize")
+    return out
+
+
+FP8L_NOALLOC_MAX_WORKSPACE = 16 << 20
+
+
+def fp8_linear_quantize_noalloc(x: torch.Tensor, rowwise: bool = False,
+                                out: Optional[Quantized] = None, stream=None,
+                                e5m2: bool = False) -> Quantized:
+    """fp8_linear_quantize with the library's per-GPU scratch array in place
+    of a workspace (the entry point allocates nothing; pass ``out`` to keep
+    this call free of allocations too)."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
+    rows, cols = x.shape
+    if out is None:
+        out = alloc_quantized(rows, cols, rowwise, x.device)
+    _check(lib().fp8_linear_quantize_noalloc(
+        _p(x), rows, cols, _scaling(rowwise, e5m2), _p(out.q), _p(out.qt), _p(out.scale),
+        _p(out.scale_t), _p(out.amax), _stream(stream)), "fp8_linear_quantize_noalloc")
     return out
 
 

@@ -22,8 +22,9 @@
  * Conventions shared by every entry point
  *  - All matrices are row-major and dense (leading dimension = #columns).
  *  - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA memory),
- *    16-byte aligned.  The caller owns every buffer; the library keeps no
- *    state between calls, allocates nothing and never synchronizes.
+ *    16-byte aligned.  The caller owns every buffer; the library allocates
+ *    nothing, never synchronizes and keeps no state between calls (apart
+ *    from fp8_linear_quantize_noalloc's per-GPU scratch array).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    asynchronously on it; results are ready when the stream reaches them.
  *    Calls on different streams may run concurrently if their buffers do not
@@ -120,6 +121,32 @@ FP8L_API int fp8_linear_quantize(const void *x, int64_t rows, int64_t cols, int 
                         void *q, void *qt, float *scale, float *scale_t,
                         float *amax_out, void *workspace, size_t workspace_bytes,
                         void *stream);
+
+/*
+ * fp8_linear_quantize without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same definition, arguments and results
+ * as fp8_linear_quantize; the partial maxima go to a scratch array that the
+ * library holds on each GPU it runs on (FP8L_NOALLOC_MAX_WORKSPACE bytes,
+ * held until the process ends) instead of a caller's workspace.  The call
+ * allocates nothing (no hipMalloc, no allocating library call).
+ *
+ *   Limit: fp8_linear_workspace_bytes(rows, cols, scaling) must not exceed
+ *   FP8L_NOALLOC_MAX_WORKSPACE (16 MiB: any tensorwise x; rowwise x up to
+ *   about 4e8 elements, e.g. [8192, 28672]); larger requests return
+ *   FP8L_EWORKSPACE before anything is enqueued.
+ *   Sharing: every call on one GPU uses that GPU's one array.  Calls that may
+ *   run at the same time on one GPU (different streams without ordering)
+ *   race on it and must be serialised by the caller (one stream, or events);
+ *   calls in stream order are safe.  Nothing in the array needs clearing:
+ *   each call writes every partial maximum it reads before reading it.
+ *   The first call on a device (with that device's stream) looks the
+ *   array's address up once; FP8L_EHIP if that fails.
+ */
+#define FP8L_NOALLOC_MAX_WORKSPACE (16u << 20)
+FP8L_API int fp8_linear_quantize_noalloc(const void *x, int64_t rows, int64_t cols, int scaling,
+                                         void *q, void *qt, float *scale, float *scale_t,
+                                         float *amax_out, void *stream);
 
 /*
  * Tensorwise amax of one bf16 matrix alone: one GPU's share of the global

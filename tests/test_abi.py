@@ -100,6 +100,35 @@ def test_quantize_rejects_bad_arguments():
 
 
 @pytestmark_cpu
+def test_quantize_noalloc_rejects_bad_arguments():
+    """The same argument rules as fp8_linear_quantize, and requests beyond the
+    scratch array's size rejected on the host (no HIP call is made)."""
+    E = ops
+    P = ctypes.c_void_p
+
+    def call(x=A16, rows=16, cols=16, scaling=0, q=A16, qt=A16, s=A16, st=A16, amax=None):
+        return ops.lib().fp8_linear_quantize_noalloc(
+            P(x) if x else None, rows, cols, scaling, P(q) if q else None,
+            P(qt) if qt else None, P(s) if s else None, P(st) if st else None,
+            P(amax) if amax else None, None)
+
+    assert call(scaling=4) == E.FP8L_EINVAL
+    assert call(rows=17) == E.FP8L_ESHAPE
+    assert call(x=None) == E.FP8L_EINVAL
+    assert call(st=None) == E.FP8L_EINVAL
+    assert call(qt=A_BAD) == E.FP8L_EALIGN
+    assert call(amax=A16 + 1) == E.FP8L_EALIGN
+    limit = ops.FP8L_NOALLOC_MAX_WORKSPACE
+    # rowwise [65536, 32768] needs ~84 MB of partial maxima
+    assert ops.fp8_linear_workspace_bytes(65536, 32768, True) > limit
+    assert call(rows=65536, cols=32768, scaling=E.FP8L_ROWWISE) == E.FP8L_EWORKSPACE
+    # the largest rowwise workloads fit
+    assert ops.fp8_linear_workspace_bytes(8192, 28672, True) <= limit
+    assert ops.fp8_linear_workspace_bytes(28672, 8192, True) <= limit
+    assert ops.fp8_linear_workspace_bytes(1 << 20, 1 << 20, False) <= limit
+
+
+@pytestmark_cpu
 def test_gemm_entry_points_reject_bad_arguments():
     E = ops
     L = ops.lib()
