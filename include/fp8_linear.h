@@ -183,7 +183,11 @@ FP8L_API int fp8_linear_quantize_scaled(const void *x, int64_t rows, int64_t col
                                         const float *scale, void *q, void *qt, void *stream);
 
 /*
- * Forward GEMM of the linear (out = X . W^T) on the quantized operands:
+ * Forward GEMM of the linear (out = X . W^T) on the quantized operands: the
+ * fp8 GEMM that is the point of the method (the forum index "torchtitan",
+ * topic "Enabling Float8 All-Gather in FSDP2": fp8 speeds up large GEMMs),
+ * with bf16 output as under the mixed-precision policy of the "torchtitan"
+ * tutorial page, Part IV, Stage 5:
  *
  *   out[m][n] = bf16( fp32( fp32(acc * (1/sx)) * (1/sw) ) ),
  *   acc       = sum_k value(xq[m][k]) * value(wq[n][k])     (fp32 accumulate)
@@ -198,7 +202,9 @@ FP8L_API int fp8_linear_fwd(const void *xq, const float *sx, const void *wq,
                    int scaling, void *out, void *stream);
 
 /*
- * Backward GEMMs of the linear on the quantized operands:
+ * Backward GEMMs of the linear on the quantized operands (the same fp8 GEMM,
+ * forum topic "Enabling Float8 All-Gather in FSDP2"; bf16 gradients as under
+ * the tutorial page's mixed-precision policy, Part IV, Stage 5):
  *
  *   grad_x[m][k] = bf16((sum_n dyq[m][n]  * wtq[k][n]) / sdy[m]  / swt[k])
  *   grad_w[n][k] = bf16((sum_m dytq[n][m] * xtq[k][m]) / sdyt[n] / sxt[k])
