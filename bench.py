@@ -250,6 +250,15 @@ def measure_ffn_block(steps, wl, stream, reps: int = 5, e5m2_grad: bool = False)
                                         "saved_frac": round(1 - fused / unfused, 4)}}
 
 
+def backlog(cycles: int = 20_000_000):
+    """Queue a short device-side spin (about 10 ms) ahead of a group of
+    timed launches, so the host enqueues them all before the device reaches
+    them: HIP events then time the kernels back to back, not host gaps
+    (an idle device records an event as soon as the host enqueues it)."""
+    import torch
+    torch.cuda._sleep(cycles)
+
+
 def measure_next_rows(steps, stream, reps: int = 5):
     """The entry points beyond the linear's own step, timed on the same FFN
     tensors after the main measurement (outside `value`): the shard amax and
@@ -272,6 +281,7 @@ def measure_next_rows(steps, stream, reps: int = 5):
         rec[kind].append((work, e0, e1))
 
     for r in range(reps + 1):
+        backlog()
         for ls in steps:
             for t, qz in ((ls.x, ls.qx), (ls.w, ls.qw), (ls.dy, ls.qdy)):
                 n = t.numel()
@@ -299,26 +309,26 @@ def measure_next_rows(steps, stream, reps: int = 5):
                 seen.add(t.data_ptr())
                 tensors.append((t, qz))
     for r in range(reps + 1):
+        backlog()
         for t, qz in tensors:
             timed("cast_hbm", 4 * t.numel(),
                   lambda: ops.fp8_linear_quantize_scaled(t, qz.scale, qz.q, qz.qt))
         if r == 0:
             torch.cuda.synchronize()
             rec["cast_hbm"].clear()
-    # reference for cast_hbm: a plain device copy of 1 GiB (torch's copy
-    # kernel; as many bytes read as written), the practical HBM rate for a
-    # stream that reads and writes in equal parts
-    rec["copy_reference"] = []
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=steps[0].x.device)
-    dst = torch.empty_like(src)
+    # the shard amax alone in the same rotation (two launches per call:
+    # partial maxima, then one workgroup reduces them into amax_out)
+    rec["amax_hbm"] = []
     for r in range(reps + 1):
-        timed("copy_reference", 2 * src.numel(), lambda: dst.copy_(src))
+        backlog()
+        for t, qz in tensors:
+            timed("amax_hbm", 2 * t.numel(),
+                  lambda: ops.fp8_linear_amax(t, amax_out, steps[0].ws))
         if r == 0:
             torch.cuda.synchronize()
-            rec["copy_reference"].clear()
+            rec["amax_hbm"].clear()
     torch.cuda.synchronize()
-    del src, dst
-    out = {}
+    out = {"stream_ceiling": measure_stream_ceiling(stream)}
     for kind, v in rec.items():
         work = sum(w for w, _, _ in v)
         ms = sum(a.elapsed_time(b) for _, a, b in v)
@@ -331,8 +341,60 @@ def measure_next_rows(steps, stream, reps: int = 5):
             ach = work / (ms * 1e-3) / 1e9
             out[kind] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                         "bytes_per_element": {"amax": 2, "copy_reference": 2}.get(kind, 4),
+                         "bytes_per_element": {"amax": 2, "amax_hbm": 2}.get(kind, 4),
                          "calls": len(v), "avg_call_us": round(ms * 1e3 / len(v), 2)}
+    ceil = out["stream_ceiling"]
+    out["amax_hbm"]["frac_of_read_ceiling"] = round(out["amax_hbm"]["achieved"]
+                                                    / ceil["read"]["achieved"], 4)
+    out["cast_hbm"]["frac_of_copy_ceiling"] = round(out["cast_hbm"]["achieved"]
+                                                    / ceil["copy"]["achieved"], 4)
+    out["amax"]["note"] = ("interleaved with the given-scale casts and fp32 grad_W GEMMs of "
+                           "the same tensors: each amax pays for the previous cast's dirty "
+                           "lines; amax_hbm is the shard amax alone")
+    return out
+
+
+def measure_stream_ceiling(stream, nbytes: int = 1 << 30, workgroups: int = 2048,
+                           reps: int = 5):
+    """Hand-written 16-byte streaming kernels (libfp8probe's fp8_probe_stream)
+    over 1 GiB buffers, four times the Infinity Cache: read only, write only,
+    and copy.  Median of reps launches each (HIP events on the launch
+    stream); they are the practical ceilings of the amax pass (read) and the
+    cast (as many bytes read as written)."""
+    import ctypes
+    import torch
+    from float8_mixed_precision_amd import build as B
+
+    L = ctypes.CDLL(B.PROBE_PATH)
+    P, i64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.fp8_probe_stream.restype = I
+    L.fp8_probe_stream.argtypes = [I, P, P, i64, I, P, P]
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    sink = torch.empty(workgroups * 256, dtype=torch.int32, device="cuda:0")
+    hs = ctypes.c_void_p(stream.cuda_stream)
+    out = {"kernel": "fp8_probe_stream: grid-stride, 16-byte accesses, 8 in flight per "
+                     "thread, %d workgroups of 256 threads" % workgroups,
+           "bytes": nbytes, "unit": "GB/s", "peak": PEAK_HBM_GBS}
+    for name, kind, factor in (("read", 0, 1), ("write", 1, 1), ("copy", 2, 2)):
+        ts = []
+        for r in range(reps + 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            backlog()
+            e0.record(stream)
+            if L.fp8_probe_stream(kind, src.data_ptr(), dst.data_ptr(), nbytes, workgroups,
+                                  sink.data_ptr(), hs) != 0:
+                raise RuntimeError("fp8_probe_stream failed")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if r:
+                ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        v = factor * nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"achieved": round(v, 1), "frac": round(v / PEAK_HBM_GBS, 4)}
+    del src, dst, sink
+    torch.cuda.empty_cache()
     return out
 
 
@@ -397,6 +459,143 @@ def measure_workload_step(name: str, reps: int = 20, warmup_s: float = 0.3,
     del steps, shared, grouped, evs
     torch.cuda.empty_cache()
     return out
+
+
+def measure_per_layout(steps, stream, reps: int = 5):
+    """Each GEMM of the step launched alone (one fp8_linear_gemm_grouped
+    problem per launch, same kernel as the step), HIP events around every
+    launch: TFLOP/s per layout (fwd X.W^T, grad_X dY.W, grad_W dY^T.X), per
+    linear and summed over the linears.  Run after the timed steps; the
+    step itself launches them grouped."""
+    import torch
+    from float8_mixed_precision_amd import ops
+    kinds = {
+        "fwd": lambda ls: (ls.qx.q, ls.qx.scale, ls.qw.q, ls.qw.scale, ls.out, ls.K),
+        "grad_x": lambda ls: (ls.qdy.q, ls.qdy.scale, ls.qw.qt, ls.qw.scale_t, ls.grad_x, ls.N),
+        "grad_w": lambda ls: (ls.qdy.qt, ls.qdy.scale_t, ls.qx.qt, ls.qx.scale_t, ls.grad_w,
+                              ls.M),
+    }
+    rec = []
+    for r in range(reps + 1):
+        backlog()
+        for li, ls in enumerate(steps):
+            for kind, f in kinds.items():
+                a, sa, b, sb, c, k = f(ls)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                ops.fp8_linear_gemm_grouped([(a, sa, b, sb, c)], ls.rowwise, stream,
+                                            e5m2=ls.e5m2_grad and kind != "fwd")
+                e1.record(stream)
+                if r:
+                    rec.append((li, kind, 2 * ls.M * ls.N * ls.K, k, e0, e1))
+        if r == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    out = {"method": "each GEMM alone, HIP events per launch, %d launches per GEMM" % reps}
+    for kind in kinds:
+        sel = [x for x in rec if x[1] == kind]
+        fl = sum(x[2] for x in sel)
+        ms = sum(x[4].elapsed_time(x[5]) for x in sel)
+        per = []
+        for li in range(len(steps)):
+            s2 = [x for x in sel if x[0] == li]
+            ms2 = sum(x[4].elapsed_time(x[5]) for x in s2)
+            per.append({"linear": li, "contraction": s2[0][3],
+                        "tflops": round(sum(x[2] for x in s2) / (ms2 * 1e-3) / 1e12, 1)})
+        out[kind] = {"tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                     "per_linear": per}
+    return out
+
+
+def collect_step_samples(steps, per_gemm: int = 1536, seed: int = 7):
+    """Host copies of what the CPU oracle needs to check the timed step's
+    results: every fp8 operand and scale as the device wrote it, the bf16
+    inputs, and sampled outputs of each GEMM (random positions plus the
+    corners of the output).  Plain data movement, no arithmetic."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(seed)
+
+    def h(t):
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    torch.cuda.synchronize()
+    lins = []
+    for ls in steps:
+        d = {"rowwise": ls.rowwise, "M": ls.M, "N": ls.N, "K": ls.K}
+        for name, qz, src in (("x", ls.qx, ls.x), ("w", ls.qw, ls.w), ("dy", ls.qdy, ls.dy)):
+            d[name] = (h(qz.q), h(qz.qt), h(qz.scale), h(qz.scale_t), h(src))
+        for kind, t in (("fwd", ls.out), ("grad_x", ls.grad_x), ("grad_w", ls.grad_w)):
+            m, n = t.shape
+            ii = np.concatenate([rng.integers(0, m, per_gemm), [0, 0, m - 1, m - 1]])
+            jj = np.concatenate([rng.integers(0, n, per_gemm), [0, n - 1, 0, n - 1]])
+            d[kind] = (ii, jj, h(t)[ii, jj])
+        lins.append(d)
+    return lins
+
+
+def step_parity(lins, rows_per_tensor: int = 8, seed: int = 11):
+    """The oracle on the timed step's data (CPU leg): the sampled GEMM outputs
+    against the oracle's GEMM on the device's own fp8 operands (relative
+    Frobenius, largest bf16 ulp distance, share within 2 ulps), and the
+    quantize of sampled rows against the oracle's (the scale from the amax
+    of the whole bf16 tensor, then the cast of those rows with it: the bytes
+    must be equal).  Tensorwise workloads check q and qt rows; rowwise
+    workloads check the scale vectors only."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(seed)
+    G, O = [], []
+    q_rows = q_bad = 0
+    for d in lins:
+        for name in ("x", "w", "dy"):
+            q, qt, sc, sct, x = d[name]
+            a = oracle.amax(x)
+            if d["rowwise"]:
+                continue
+            s_or = oracle.scale_from_amax(a)
+            if np.float32(s_or).view(np.uint32) != sc.view(np.uint32)[0]:
+                q_bad += 1
+            rows = rng.integers(0, x.shape[0], rows_per_tensor)
+            for r in rows:
+                rq, _ = oracle.quantize_scaled(x[r:r + 1], sc[0])
+                q_rows += 1
+                q_bad += int(not np.array_equal(rq.ravel(), q[r]))
+            # columns of x = rows of qt
+            cols = rng.integers(0, x.shape[1], rows_per_tensor)
+            for c in cols:
+                q_rows += 1
+                q_bad += int(not np.array_equal(q[:, c], qt[c]))
+        operands = {"fwd": (d["x"][0], d["x"][2], d["w"][0], d["w"][2]),
+               "grad_x": (d["dy"][0], d["dy"][2], d["w"][1], d["w"][3]),
+               "grad_w": (d["dy"][1], d["dy"][3], d["x"][1], d["x"][3])}
+        for kind, (a, sa, b, sb) in operands.items():
+            ii, jj, g = d[kind]
+            O.append(oracle.gemm_tn_sampled(a, sa, b, sb, ii, jj))
+            G.append(g)
+    G = np.concatenate(G)
+    O = np.concatenate(O)
+    dist = oracle.bf16_ulp_distance(G, O)
+    return {"gemm_outputs_sampled": int(len(G)),
+            "relfro": float("%.3g" % oracle.rel_frobenius(G, O)),
+            "max_ulp": int(dist.max()), "frac_le2": round(float(np.mean(dist <= 2)), 6),
+            "quantize_rows_checked": q_rows, "quantize_rows_differing": q_bad,
+            "note": "GEMM outputs of the last timed step against the oracle's GEMM on the "
+                    "device's fp8 operands; quantize rows (and q/qt transposes) against the "
+                    "oracle's cast with the scale of the tensor's amax"}
+
+
+def environment():
+    """ROCm / HIP version, the device's architecture and compute units."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"hip": torch.version.hip, "torch": torch.__version__,
+            "gfx_arch": getattr(p, "gcnArchName", None), "device": p.name,
+            "compute_units": p.multi_processor_count}
 
 
 def measure_mfma_ceiling(codes, stream, target_ms: float = 25.0, launches: int = 4):
@@ -635,6 +834,9 @@ def main():
     quant_gbs = q_bytes / (q_ms * 1e-3) / 1e9
     value = wl.flops * args.steps / elapsed / 1e12
 
+    # host copies of the last timed step's operands and sampled outputs, for
+    # the oracle's check in the CPU leg
+    samples = None if args.no_cpu_baseline else collect_step_samples(steps)
     traffic = measured_traffic(wl.name)
     result = {
         "metric": "fp8 linear fwd+bwd TFLOP/s at Llama-3.1-8B FFN shape; % fp8 MFMA peak",
@@ -674,7 +876,11 @@ def main():
         "time_split_ms_per_step": {"gemm": round(g_ms / args.steps, 4),
                                    "quantize": round(q_ms / args.steps, 4)},
         "cpu_baseline": None,
+        "parity": None,
+        "environment": environment(),
     }
+    print("[bench] per-layout GEMM rates", file=sys.stderr, flush=True)
+    result["gemm_per_layout"] = measure_per_layout(steps, stream)
     if not args.no_next_rows:
         print("[bench] MFMA-only ceiling", file=sys.stderr, flush=True)
         ceil = measure_mfma_ceiling(steps[0].qx.q, stream)
@@ -708,6 +914,9 @@ def main():
     del steps, shared, grouped
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
+        print("[bench] cpu oracle: parity of the timed step", file=sys.stderr, flush=True)
+        result["parity"] = step_parity(samples)
+        del samples
         print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
     print(json.dumps(result), flush=True)

@@ -11,8 +11,9 @@ LIB_DIR = os.path.join(HERE, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libfp8linear.so")
 SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "swiglu.hip"]
 # measurement support, kept out of the method's library: the MFMA-only
-# throughput probe that bench.py reports beside the GEMM's roofline
-PROBE_SOURCES = ["mfma_probe.hip"]
+# throughput and one-instruction probes, and the HBM streaming probes that
+# bench.py reports beside the rooflines
+PROBE_SOURCES = ["mfma_probe.hip", "stream_probe.hip"]
 PROBE_PATH = os.path.join(LIB_DIR, "libfp8probe.so")
 # measurement support: the library again, with per-workgroup phase
 # timestamps in the GEMM (bench.py --phase-timing)

@@ -36,6 +36,21 @@ constexpr int TW_CHUNK = AM_THREADS * TW_UNROLL;   // 16-byte vectors per chunk
 // cast tile: 128 rows x 128 columns per 256-thread workgroup.
 constexpr int CT_T = 128;
 constexpr int CT_THREADS = 256;
+// Tile order of the cast: groups of CT_GROUP row tiles, the row tile
+// fastest within a group, so the workgroups running at one time write
+// neighbouring 128-byte segments of each qt row.  q and qt are written with
+// non-temporal stores when CT_NT.  (Both are set from measurements of the
+// whole step; see the notes at k_cast_transpose.)
+#ifndef FP8L_CAST_GROUP
+#define FP8L_CAST_GROUP 4
+#endif
+#ifndef FP8L_CAST_NT
+#define FP8L_CAST_NT 0
+#endif
+constexpr int CT_GROUP = FP8L_CAST_GROUP;
+constexpr bool CT_NT = FP8L_CAST_NT != 0;
+typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 
 // ----------------------------------------------------------------- amax --
 //
@@ -264,8 +279,15 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
     uint8_t *__restrict__ q, uint8_t *__restrict__ qt) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[CT_T * CT_T];
   const int tid = threadIdx.x;
-  const int tile_c = blockIdx.x % tiles_c;
-  const int tile_r = blockIdx.x / tiles_c;
+  // block -> (tile_r, tile_c): groups of CT_GROUP row tiles (the last one
+  // possibly shorter), row tile fastest within a group
+  const int tiles_r = (rows + CT_T - 1) / CT_T;
+  const int per_group = CT_GROUP * tiles_c;
+  const int first_r = ((int)blockIdx.x / per_group) * CT_GROUP;
+  const int gm = min(tiles_r - first_r, CT_GROUP);
+  const int in_group = (int)blockIdx.x % per_group;
+  const int tile_r = first_r + in_group % gm;
+  const int tile_c = in_group / gm;
   const int r0 = tile_r * CT_T;
   const int c0 = tile_c * CT_T;
   const int c8 = tid & 15;
@@ -335,7 +357,11 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
         const float s = srs[j];
         const uint32_t q0 = fp8x4<FMT>(f[0] * s, f[1] * s, f[2] * s, f[3] * s);
         const uint32_t q1 = fp8x4<FMT>(f[4] * s, f[5] * s, f[6] * s, f[7] * s);
-        *reinterpret_cast<uint2 *>(q + (size_t)(r + j) * cols + c) = make_uint2(q0, q1);
+        v2u_t *qdst = reinterpret_cast<v2u_t *>(q + (size_t)(r + j) * cols + c);
+        if (CT_NT)
+          __builtin_nontemporal_store((v2u_t){q0, q1}, qdst);
+        else
+          *qdst = (v2u_t){q0, q1};
         if (ROWWISE) {
           lo[j] = fp8x4<FMT>(f[0] * sc[0], f[1] * sc[1], f[2] * sc[2], f[3] * sc[3]);
           hi[j] = fp8x4<FMT>(f[4] * sc[4], f[5] * sc[5], f[6] * sc[6], f[7] * sc[7]);
@@ -378,8 +404,12 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
     const int gr = r0 + rc * 16;
     if (gc < cols && gr < rows) {
       const int pc = rc ^ ((col >> 3) & 7);
-      const uint4 v = *reinterpret_cast<const uint4 *>(lds + col * CT_T + pc * 16);
-      *reinterpret_cast<uint4 *>(qt + (size_t)gc * rows + gr) = v;
+      const v4u_t v = *reinterpret_cast<const v4u_t *>(lds + col * CT_T + pc * 16);
+      v4u_t *tdst = reinterpret_cast<v4u_t *>(qt + (size_t)gc * rows + gr);
+      if (CT_NT)
+        __builtin_nontemporal_store(v, tdst);
+      else
+        *tdst = v;
     }
   }
 }
