@@ -76,6 +76,11 @@
 // apart; the parity tests bound that difference per element.
 #include "fp8l_internal.h"
 
+// 1: the persistent kernel (k_gemm_fp8_pers), 0: one workgroup per tile
+#ifndef FP8L_GEMM_PERSISTENT
+#define FP8L_GEMM_PERSISTENT 1
+#endif
+
 namespace fp8l {
 #ifdef FP8L_PHASE_TIMING
 // Measurement build only (a separate library compiled with
@@ -141,13 +146,16 @@ __device__ __forceinline__ void barrier_lds() {
 // reads across it nor inserts waits of its own; completion is tracked with
 // explicit vmcnt waits.  m0 is named as clobbered (nothing else in this
 // kernel uses it); clang warns that it does not track reserved registers.
+// The LDS address is wave-uniform; readfirstlane keeps it in a scalar
+// register where the compiler has placed it in a vector one (it folds away
+// where the value is already scalar).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr,
                                       uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff)
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rs), "s"(soff)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -186,6 +194,7 @@ struct GemmGroup {
   int M[MAX_GROUP], N[MAX_GROUP], K[MAX_GROUP];
   int tiles_m[MAX_GROUP], tiles_n[MAX_GROUP], first[MAX_GROUP];
   int count;
+  int total;   // tiles of all problems
 };
 
 // element i of a kernel-argument array for a wave-uniform i (selects, so the
@@ -623,6 +632,477 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(GemmGroup g) {
 #endif
 }
 
+// ---------------------------------------------------------------------------
+// Persistent form.  One workgroup per compute unit (gridDim.x = G =
+// min(tiles, compute units)); each workgroup walks a fixed list of tiles
+// (decode_tile), so the per-tile launch cost and the pipeline fill are paid
+// once per workgroup instead of once per tile.  One DMA stream runs two
+// k-tiles ahead of the MFMAs across tile boundaries: the next tile's first
+// two k-tiles load during the current tile's last two, and its first
+// fragments are read at the top of the tile, so a tile starts without a
+// prologue.  The epilogue stages through its own 32 KB LDS region (4 passes
+// of 32 rows per wave, 16-byte chunks XOR-swizzled by row instead of
+// padding), so it never touches the operand stages that are filling for the
+// next tile; it leaves its stores in flight while the next tile's first
+// k-tile starts, and clears each accumulator block once it is stored.
+// Nothing is shared between workgroups: correctness does not depend on how
+// many are resident at once.
+constexpr int EPI_OFF = 2 * STAGE_BYTES;        // 128 KB
+constexpr int EPI_WAVE_BYTES = 8 * 1024;        // per wave: 32 rows x 256 B
+constexpr int EPI_BYTES = 4 * EPI_WAVE_BYTES;   // 32 KB (rowwise: inverse scales first)
+static_assert(INV_BYTES <= EPI_BYTES, "inverse scales fit the epilogue region");
+// epilogue stores left in flight when the next tile's first k-tile waits for
+// its operands (bf16: 4 passes x 8 stores per lane)
+constexpr int EPI_STORES = 32;
+
+// s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Tile i (i = 0, 1, ...) of persistent workgroup b.  Workgroups are dealt
+// to the XCDs round-robin (b on XCD b % 8), and each XCD works through its
+// own contiguous share of every problem's grouped tile order, problem after
+// problem, as the XCD's blocks would with one workgroup per tile
+// (tile_of_block): its nx workgroups take positions l, l + nx, l + 2 nx, ...
+// (l = b / 8) of that sequence, so the tiles an XCD runs at one time are
+// neighbours in the grouped order and share operand panels in its L2.
+struct TileCoord {
+  int pi, m0, n0;
+  bool valid;
+};
+__device__ __forceinline__ TileCoord decode_tile(const GemmGroup &g, int b, int i, int G) {
+  const int x = b % NUM_XCD;
+  const int nx = (G - x + NUM_XCD - 1) / NUM_XCD;   // workgroups on XCD x
+  int s = b / NUM_XCD + i * nx;                      // position in XCD x's sequence
+  for (int pi = 0; pi < g.count; ++pi) {
+    const int tiles_m = pick(g.tiles_m, pi), tiles_n = pick(g.tiles_n, pi);
+    const int T = tiles_m * tiles_n;
+    const int cnt = (T - x + NUM_XCD - 1) / NUM_XCD;  // XCD x's share of problem pi
+    if (s < cnt) {
+      int base = 0;
+      for (int xx = 0; xx < x; ++xx) base += (T - xx + NUM_XCD - 1) / NUM_XCD;
+      const int q = base + s;                        // grouped order index
+      const int group = GROUP_M * tiles_n;
+      const int first_m = (q / group) * GROUP_M;
+      const int gm = min(tiles_m - first_m, GROUP_M);
+      const int in_group = q % group;
+      return {pi, (first_m + in_group % gm) * BM, (in_group / gm) * BN, true};
+    }
+    s -= cnt;
+  }
+  return {0, 0, 0, false};
+}
+
+template <bool KFULL, bool RW, bool F32, int FA, bool ACC>
+__global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
+  static_assert(!(F32 && ACC), "accumulation is into a bf16 output");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[EPI_OFF + EPI_BYTES];
+  const int G = gridDim.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
+  const uint32_t wave_dst = lds_base + (uint32_t)(wave * 64 * BK);
+
+  // ---- DMA cursor: the unit (tile, k-tile) whose operands load next.  Wave
+  // w, instruction q (0..7 A, 8..15 B) fills slab rows w*64 + (q&7)*8 +
+  // lane/8, chunk (lane%8) ^ (lane/8) ^ (q&1), as in k_gemm_fp8_tn.  The
+  // tile's first row is in the buffer resource (base A + m0 K, M - m0 rows),
+  // so the per-lane offsets depend only on K, and rows past the matrix fail
+  // the bounds check on the vector offset alone (they read as zero).
+  const int lr = lane >> 3;
+  const int c_even = (lane & 7) ^ lr;
+  const int c_odd = c_even ^ 1;
+  int d_tile = 0, d_kt = 0, d_nk = 0, d_K = -1;     // d_tile: this workgroup's tile index
+  bool d_valid = true;
+  __amdgpu_buffer_rsrc_t d_rsA, d_rsB;
+  uint32_t voff[16];
+  // per-lane offsets for the cursor's K, from an opaque copy of the lane
+  // index (recomputed where needed rather than kept live or spilled)
+  auto set_voff = [&]() {
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
+    const int lr_v = lane_v >> 3;
+    const int ce_v = (lane_v & 7) ^ lr_v;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = wave * 64 + (q & 7) * 8 + lr_v;
+      voff[q] = (uint32_t)(row * d_K + ((q & 1) ? ce_v ^ 1 : ce_v) * 16);
+    }
+  };
+  auto d_setup = [&]() {
+    TileCoord tc = decode_tile(g, blockIdx.x, d_tile, G);
+    d_valid = tc.valid;
+    if (!d_valid) tc = decode_tile(g, 0, 0, G);
+    const int M = pick(g.M, tc.pi), N = pick(g.N, tc.pi);
+    const int K = pick(g.K, tc.pi);
+    d_nk = (K + BK - 1) / BK;
+    // an exhausted cursor still issues its (zero-filling) transfers into
+    // the stage no one reads any more: an empty buffer
+    d_rsA = __builtin_amdgcn_make_buffer_rsrc((void *)(pick(g.A, tc.pi) + (size_t)tc.m0 * K),
+                                              (short)0, d_valid ? (M - tc.m0) * K : 0,
+                                              0x00020000);
+    d_rsB = __builtin_amdgcn_make_buffer_rsrc((void *)(pick(g.B, tc.pi) + (size_t)tc.n0 * K),
+                                              (short)0, d_valid ? (N - tc.n0) * K : 0,
+                                              0x00020000);
+    if (K != d_K) {
+      d_K = K;
+      set_voff();
+    }
+  };
+  auto d_advance = [&]() {
+    if (!d_valid) return;
+    if (++d_kt == d_nk) {
+      d_kt = 0;
+      ++d_tile;
+      d_setup();
+    }
+  };
+  d_setup();
+
+#define FP8P_DMA1(STAGE, Q)                                                       \
+  do {                                                                            \
+    const uint32_t k0_ = (uint32_t)(d_kt * BK);                                   \
+    const bool kok_ = KFULL || (int)k0_ + (((Q) & 1) ? c_odd : c_even) * 16 < d_K; \
+    const uint32_t dst_ = wave_dst + (uint32_t)((STAGE) * STAGE_BYTES +           \
+                          ((Q) >= 8 ? SLAB : 0) + ((Q) & 7) * 1024);              \
+    dma16((Q) >= 8 ? d_rsB : d_rsA, dst_, kok_ ? voff[Q] : OOB, k0_);             \
+  } while (0)
+
+  // ---- fragment reads (as in k_gemm_fp8_tn); the per-lane offsets are
+  // set at the top of each tile
+  int fArow, fBrow, fc0, fc1;
+  v8i fa[NF], fb[NF];
+  v4f acc[NF][NF];   // [j: n block][i: m block]
+
+#define FP8P_RD(STAGE, X, F, H)                                                   \
+  do {                                                                            \
+    const uint8_t *src_ = lds + (STAGE) * STAGE_BYTES +                           \
+                          ((X) ? fBrow : fArow) + (F) * FR * BK + ((H) ? fc1 : fc0); \
+    const v4u v_ = *reinterpret_cast<const v4u *>(src_);                          \
+    if (X) { fb[F][4 * (H)] = (int)v_.x; fb[F][4 * (H) + 1] = (int)v_.y;          \
+             fb[F][4 * (H) + 2] = (int)v_.z; fb[F][4 * (H) + 3] = (int)v_.w; }    \
+    else   { fa[F][4 * (H)] = (int)v_.x; fa[F][4 * (H) + 1] = (int)v_.y;          \
+             fa[F][4 * (H) + 2] = (int)v_.z; fa[F][4 * (H) + 3] = (int)v_.w; }    \
+  } while (0)
+  // MFMA of block (J, I)
+#define FP8P_MF(J, I)                                                             \
+  acc[J][I] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                   \
+      fb[J], fa[I], acc[J][I], 0, FA, 0, 0, 0, 0)
+#define FP8P_M(S, I0) FP8P_MF((S) / 4, (I0) + ((((S) / 4) & 1) ? (S) % 4 : 3 - (S) % 4));
+#define FP8P_E() __builtin_amdgcn_sched_barrier(0);
+#define FP8P_H1(ST) \
+  FP8P_M(0, 0) FP8P_RD(ST, 0, 7, 0); FP8P_E() \
+  FP8P_M(1, 0) FP8P_RD(ST, 0, 7, 1); FP8P_E() \
+  FP8P_M(2, 0) FP8P_RD(ST, 0, 6, 0); FP8P_E() \
+  FP8P_M(3, 0) FP8P_RD(ST, 0, 6, 1); FP8P_E() \
+  FP8P_M(4, 0) FP8P_RD(ST, 0, 5, 0); FP8P_E() \
+  FP8P_M(5, 0) FP8P_RD(ST, 0, 5, 1); FP8P_E() \
+  FP8P_M(6, 0) FP8P_RD(ST, 0, 4, 0); FP8P_E() \
+  FP8P_M(7, 0) FP8P_RD(ST, 0, 4, 1); FP8P_E() \
+  FP8P_M(8, 0) FP8P_RD(ST, 1, 7, 0); FP8P_E() \
+  FP8P_M(9, 0) FP8P_RD(ST, 1, 7, 1); FP8P_E() \
+  FP8P_M(10, 0) FP8P_E() FP8P_M(11, 0) FP8P_E() FP8P_M(12, 0) FP8P_E() \
+  FP8P_M(13, 0) FP8P_E() FP8P_M(14, 0) FP8P_E() FP8P_M(15, 0) FP8P_E() \
+  FP8P_M(16, 0) FP8P_E() FP8P_M(17, 0) FP8P_E() FP8P_M(18, 0) FP8P_E() \
+  FP8P_M(19, 0) FP8P_E() FP8P_M(20, 0) FP8P_E() FP8P_M(21, 0) FP8P_E() \
+  FP8P_M(22, 0) FP8P_E() FP8P_M(23, 0) FP8P_E() FP8P_M(24, 0) FP8P_E() \
+  FP8P_M(25, 0) FP8P_E() FP8P_M(26, 0) FP8P_E() FP8P_M(27, 0) FP8P_E() \
+  FP8P_M(28, 0) FP8P_E() FP8P_M(29, 0) FP8P_E() FP8P_M(30, 0) FP8P_E() \
+  FP8P_M(31, 0) FP8P_E()
+#define FP8P_H2(STN, DST) \
+  FP8P_M(0, 4) FP8P_RD(STN, 0, 3, 0); FP8P_E() \
+  FP8P_M(1, 4) FP8P_DMA1(DST, 0); FP8P_E() \
+  FP8P_M(2, 4) FP8P_RD(STN, 0, 3, 1); FP8P_E() \
+  FP8P_M(3, 4) FP8P_DMA1(DST, 1); FP8P_E() \
+  FP8P_M(4, 4) FP8P_RD(STN, 0, 2, 0); FP8P_RD(STN, 1, 0, 0); FP8P_E() \
+  FP8P_M(5, 4) FP8P_RD(STN, 1, 0, 1); FP8P_DMA1(DST, 2); FP8P_E() \
+  FP8P_M(6, 4) FP8P_RD(STN, 0, 2, 1); FP8P_E() \
+  FP8P_M(7, 4) FP8P_DMA1(DST, 3); FP8P_E() \
+  FP8P_M(8, 4) FP8P_RD(STN, 0, 1, 0); FP8P_RD(STN, 1, 1, 0); FP8P_E() \
+  FP8P_M(9, 4) FP8P_RD(STN, 1, 1, 1); FP8P_DMA1(DST, 4); FP8P_E() \
+  FP8P_M(10, 4) FP8P_RD(STN, 0, 1, 1); FP8P_E() \
+  FP8P_M(11, 4) FP8P_DMA1(DST, 5); FP8P_E() \
+  FP8P_M(12, 4) FP8P_RD(STN, 0, 0, 0); FP8P_RD(STN, 1, 2, 0); FP8P_E() \
+  FP8P_M(13, 4) FP8P_RD(STN, 1, 2, 1); FP8P_DMA1(DST, 6); FP8P_E() \
+  FP8P_M(14, 4) FP8P_RD(STN, 0, 0, 1); FP8P_E() \
+  FP8P_M(15, 4) FP8P_DMA1(DST, 7); FP8P_E() \
+  FP8P_M(16, 4) FP8P_RD(STN, 1, 3, 0); FP8P_E() \
+  FP8P_M(17, 4) FP8P_RD(STN, 1, 3, 1); FP8P_DMA1(DST, 8); FP8P_E() \
+  FP8P_M(18, 4) FP8P_E() \
+  FP8P_M(19, 4) FP8P_DMA1(DST, 9); FP8P_E() \
+  FP8P_M(20, 4) FP8P_RD(STN, 1, 4, 0); FP8P_E() \
+  FP8P_M(21, 4) FP8P_RD(STN, 1, 4, 1); FP8P_DMA1(DST, 10); FP8P_E() \
+  FP8P_M(22, 4) FP8P_E() \
+  FP8P_M(23, 4) FP8P_DMA1(DST, 11); FP8P_E() \
+  FP8P_M(24, 4) FP8P_RD(STN, 1, 5, 0); FP8P_E() \
+  FP8P_M(25, 4) FP8P_RD(STN, 1, 5, 1); FP8P_DMA1(DST, 12); FP8P_E() \
+  FP8P_M(26, 4) FP8P_E() \
+  FP8P_M(27, 4) FP8P_DMA1(DST, 13); FP8P_E() \
+  FP8P_M(28, 4) FP8P_RD(STN, 1, 6, 0); FP8P_E() \
+  FP8P_M(29, 4) FP8P_RD(STN, 1, 6, 1); FP8P_DMA1(DST, 14); FP8P_E() \
+  FP8P_M(30, 4) FP8P_E() \
+  FP8P_M(31, 4) FP8P_DMA1(DST, 15); FP8P_E()
+
+// last k-tile of a tile: the DMAs only (the next tile's first fragments are
+// read after the epilogue, which keeps them out of its registers)
+#define FP8P_H2D(DST) \
+  FP8P_M(0, 4) FP8P_E() FP8P_M(1, 4) FP8P_DMA1(DST, 0); FP8P_E() \
+  FP8P_M(2, 4) FP8P_E() FP8P_M(3, 4) FP8P_DMA1(DST, 1); FP8P_E() \
+  FP8P_M(4, 4) FP8P_E() FP8P_M(5, 4) FP8P_DMA1(DST, 2); FP8P_E() \
+  FP8P_M(6, 4) FP8P_E() FP8P_M(7, 4) FP8P_DMA1(DST, 3); FP8P_E() \
+  FP8P_M(8, 4) FP8P_E() FP8P_M(9, 4) FP8P_DMA1(DST, 4); FP8P_E() \
+  FP8P_M(10, 4) FP8P_E() FP8P_M(11, 4) FP8P_DMA1(DST, 5); FP8P_E() \
+  FP8P_M(12, 4) FP8P_E() FP8P_M(13, 4) FP8P_DMA1(DST, 6); FP8P_E() \
+  FP8P_M(14, 4) FP8P_E() FP8P_M(15, 4) FP8P_DMA1(DST, 7); FP8P_E() \
+  FP8P_M(16, 4) FP8P_E() FP8P_M(17, 4) FP8P_DMA1(DST, 8); FP8P_E() \
+  FP8P_M(18, 4) FP8P_E() FP8P_M(19, 4) FP8P_DMA1(DST, 9); FP8P_E() \
+  FP8P_M(20, 4) FP8P_E() FP8P_M(21, 4) FP8P_DMA1(DST, 10); FP8P_E() \
+  FP8P_M(22, 4) FP8P_E() FP8P_M(23, 4) FP8P_DMA1(DST, 11); FP8P_E() \
+  FP8P_M(24, 4) FP8P_E() FP8P_M(25, 4) FP8P_DMA1(DST, 12); FP8P_E() \
+  FP8P_M(26, 4) FP8P_E() FP8P_M(27, 4) FP8P_DMA1(DST, 13); FP8P_E() \
+  FP8P_M(28, 4) FP8P_E() FP8P_M(29, 4) FP8P_DMA1(DST, 14); FP8P_E() \
+  FP8P_M(30, 4) FP8P_E() FP8P_M(31, 4) FP8P_DMA1(DST, 15); FP8P_E()
+
+  // ---- the first two units' operands (the fragments are read at the top
+  // of each tile)
+  if (d_valid) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) FP8P_DMA1(0, q);
+    d_advance();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) FP8P_DMA1(1, q);
+    d_advance();
+  }
+  wait_vmcnt0();
+  barrier_lds();
+
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  uint8_t *epi = lds + EPI_OFF + wave * EPI_WAVE_BYTES;
+  const float *inv = reinterpret_cast<const float *>(lds + EPI_OFF);
+  int st = 0;          // stage of the current unit
+#pragma unroll
+  for (int j = 0; j < NF; ++j)
+#pragma unroll
+    for (int i = 0; i < NF; ++i) acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int tile = 0;; ++tile) {
+    const TileCoord tc = decode_tile(g, blockIdx.x, tile, G);
+    if (!tc.valid) break;
+    const int pi = tc.pi, m0 = tc.m0, n0 = tc.n0;
+    const int M = pick(g.M, pi), N = pick(g.N, pi), K = pick(g.K, pi);
+    const int nk = (K + BK - 1) / BK;
+    const float *__restrict__ sa = pick(g.sa, pi);
+    const float *__restrict__ sb = pick(g.sb, pi);
+#ifdef FP8L_PHASE_TIMING
+    const unsigned long long ph_t0 = __builtin_amdgcn_s_memtime();
+    const unsigned long long ph_r0 = __builtin_amdgcn_s_memrealtime();
+    unsigned long long ph_ta = ph_t0, ph_ra = ph_r0;
+#endif
+    // rowwise: the tile's 512 reciprocal scales into the epilogue region
+    // (free since the previous tile's closing barrier; read after the next
+    // barrier)
+    if (RW) {
+      float *w = reinterpret_cast<float *>(lds + EPI_OFF);
+      w[tid] = m0 + tid < M ? 1.0f / sa[m0 + tid] : 0.f;
+      w[BM + tid] = n0 + tid < N ? 1.0f / sb[n0 + tid] : 0.f;
+    }
+    // the cursor's per-lane offsets, recomputed here from an opaque copy of
+    // the lane index instead of being kept (or spilled) across the epilogue
+    set_voff();
+    {
+      int lane_v = lane;
+      asm volatile("" : "+v"(lane_v));
+      // fragment f of A: rows wm*128 + f*16 + lane%16; lane reads logical
+      // chunks 2(lane/16) and 2(lane/16)+1, swizzled by h(row)
+      const int hr = (lane_v & 7) ^ ((lane_v >> 3) & 1);
+      const int g4 = lane_v >> 4;
+      fArow = (wm * WM + (lane_v & 15)) * BK;
+      fBrow = SLAB + (wn * WN + (lane_v & 15)) * BK;
+      fc0 = ((2 * g4) ^ hr) << 4;
+      fc1 = ((2 * g4 + 1) ^ hr) << 4;
+    }
+    if (nk > 0) {
+      // A0-3 and B0-6 of the tile's first k-tile (complete in stage st: this
+      // wave waited for its part and passed a barrier since)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) { FP8P_RD(st, 0, f, 0); FP8P_RD(st, 0, f, 1); }
+#pragma unroll
+      for (int f = 0; f < 7; ++f) { FP8P_RD(st, 1, f, 0); FP8P_RD(st, 1, f, 1); }
+      // the accumulators hold zeros here: cleared before the first tile and
+      // by the previous tile's epilogue as it read them (one definition
+      // reaches the loop, so every accumulator block stays in its AGPRs)
+      // every k-tile but the last reads the next one's first fragments and
+      // loads the one after.  The first waits for its successor's operands,
+      // issued before the previous tile's epilogue, whose stores may still be
+      // in flight behind them (vmcnt counts in issue order): all but those.
+      for (int t = 0; t < nk - 1; ++t) {
+        FP8P_H1(st)
+        if (t == 0 && !F32)
+          wait_vmcnt<EPI_STORES>();
+        else
+          wait_vmcnt0();
+        wait_lgkm0();
+        barrier_lds();
+        FP8P_H2(st ^ 1, st)
+        d_advance();
+        st ^= 1;
+#ifdef FP8L_PHASE_TIMING
+        if (t == 0) {
+          ph_ta = __builtin_amdgcn_s_memtime();
+          ph_ra = __builtin_amdgcn_s_memrealtime();
+        }
+#endif
+      }
+      FP8P_H1(st)
+      if (nk == 1 && !F32)
+        wait_vmcnt<EPI_STORES>();
+      else
+        wait_vmcnt0();
+      wait_lgkm0();
+      barrier_lds();
+      FP8P_H2D(st)
+      d_advance();
+      st ^= 1;
+    } else {
+      if (RW) barrier_lds();                      // the inverse scales are written
+    }
+#ifdef FP8L_PHASE_TIMING
+    const unsigned long long ph_t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long ph_r1 = __builtin_amdgcn_s_memrealtime();
+#endif
+
+    // ---- epilogue: scale, round, stage 32 rows of the wave's 128 x 128 tile
+    // at a time in the wave's 8 KB (row r's 16-byte chunk c at c ^ (r % 16)),
+    // write whole rows
+    const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+        pick(g.C, pi), (short)0, M * N * (F32 ? 4 : 2), 0x00020000);
+    int tid_e = tid;
+    asm volatile("" : "+v"(tid_e));
+    const int lane_e = tid_e & 63;
+    const int ml16 = lane_e & 15;                 // row within a 16-row block
+    const int nq = (lane_e >> 4) * 4;             // first of the lane's 4 columns in a block
+    const float inv_a0 = RW ? 0.f : 1.0f / sa[0];
+    const float inv_b0 = RW ? 0.f : 1.0f / sb[0];
+    float inv_ar[NF];
+    v4f inv_br[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      inv_ar[f] = RW ? inv[wm * WM + f * FR + ml16] : inv_a0;
+      inv_br[f] = (v4f){inv_b0, inv_b0, inv_b0, inv_b0};
+      if (RW) inv_br[f] = *reinterpret_cast<const v4f *>(inv + BM + wn * WN + f * FR + nq);
+    }
+    if (RW) barrier_lds();                        // every wave holds its scales
+    if (F32) {
+      // one 16-row block per pass: 16 rows x 512 B (32 chunks per row)
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          const v4f ib = inv_br[j];
+          const v4f v = {(acc[j][i][0] * inv_ar[i]) * ib[0], (acc[j][i][1] * inv_ar[i]) * ib[1],
+                         (acc[j][i][2] * inv_ar[i]) * ib[2], (acc[j][i][3] * inv_ar[i]) * ib[3]};
+          acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};    // cleared for the next tile
+          const int ch = (j * 4 + (lane_e >> 4)) ^ ml16;
+          *reinterpret_cast<v4f *>(epi + ml16 * 512 + ch * 16) = v;
+        }
+        const int row0 = m0 + wm * WM + i * FR;
+        const int col = n0 + wn * WN + (lane_e & 31) * 4;
+        const bool col_ok = col < N;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int r = u * 2 + (lane_e >> 5);
+          const v4u v = *reinterpret_cast<const v4u *>(
+              epi + r * 512 + (((lane_e & 31) ^ (r & 15)) * 16));
+          const uint32_t off = (col_ok && row0 + r < M) ? (uint32_t)(((row0 + r) * N + col) * 4)
+                                                        : OOB_C;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, C_STORE_AUX);
+        }
+      }
+    } else {
+      const int scol = n0 + wn * WN + (lane_e & 15) * 8;
+      const bool col_ok = scol < N;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * p + ii;
+          const int ml = ii * FR + ml16;          // row within the pass
+#pragma unroll
+          for (int j = 0; j < NF; ++j) {
+            const v4f ib = inv_br[j];
+            const float ia = inv_ar[i];
+            f32x2 v01 = {(acc[j][i][0] * ia) * ib[0], (acc[j][i][1] * ia) * ib[1]};
+            f32x2 v23 = {(acc[j][i][2] * ia) * ib[2], (acc[j][i][3] * ia) * ib[3]};
+            acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};  // cleared for the next tile
+            const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
+            const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
+            // byte column (j*16 + nq)*2: chunk 2j + nq/8, 8 bytes in at (nq%8)*2
+            const int ch = (2 * j + (nq >> 3)) ^ ml16;
+            *reinterpret_cast<uint2 *>(epi + ml * 256 + ch * 16 + (nq & 7) * 2) =
+                make_uint2(p01, p23);
+          }
+        }
+        // 8 instructions: rows u*4 + lane/16 of the pass, 8 columns each
+        const int srow = m0 + wm * WM + p * 32 + (lane_e >> 4);
+        v4u v[8];
+        uint32_t off[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int r = u * 4 + (lane_e >> 4);
+          v[u] = *reinterpret_cast<const v4u *>(epi + r * 256 + (((lane_e & 15) ^ (r & 15)) * 16));
+          const bool ok = col_ok && srow + u * 4 < M;
+          off[u] = ok ? (uint32_t)(((srow + u * 4) * N + scol) * 2) : OOB_C;
+        }
+        if (ACC) {
+          v4u cin[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) cin[u] = __builtin_amdgcn_raw_buffer_load_b128(rsC, off[u], 0, 0);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const uint32_t x = v[u][d], y = cin[u][d];
+              const f32x2 sum = {__uint_as_float(x << 16) + __uint_as_float(y << 16),
+                                 __uint_as_float(x & 0xFFFF0000u) + __uint_as_float(y & 0xFFFF0000u)};
+              v[u][d] = __builtin_bit_cast(uint32_t, __builtin_convertvector(sum, bf16x2));
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off[u], 0, C_STORE_AUX);
+      }
+    }
+#ifdef FP8L_PHASE_TIMING
+    const int slot = tile * G + (int)blockIdx.x;    // round-major record index
+    if (tid == 0 && slot < PHASE_MAX_BLOCKS) {
+      const unsigned long long ph_t2 = __builtin_amdgcn_s_memtime();
+      const unsigned long long ph_r2 = __builtin_amdgcn_s_memrealtime();
+      unsigned long long *d = g_phase + (size_t)slot * 8;
+      d[0] = ph_t0; d[1] = ph_r0; d[2] = ph_ta; d[3] = ph_ra;
+      d[4] = ph_t1; d[5] = ph_r1; d[6] = ph_t2; d[7] = ph_r2;
+    }
+#endif
+    // every wave is done with the epilogue region before the next tile's
+    // inverse scales overwrite it
+    wait_lgkm0();
+    barrier_lds();
+  }
+#undef FP8P_H2D
+#undef FP8P_H2
+#undef FP8P_H1
+#undef FP8P_E
+#undef FP8P_M
+#undef FP8P_MF
+#undef FP8P_RD
+#undef FP8P_DMA1
+}
+
 }  // namespace
 
 namespace {
@@ -652,11 +1132,23 @@ hipError_t launch_group(const GemmDesc *d, int count, int rowwise, hipStream_t s
     kfull = kfull && d[i].K % BK == 0;
   }
   if (blocks == 0) return hipSuccess;
+  g.total = blocks;
+#if FP8L_GEMM_PERSISTENT
+  // one workgroup per compute unit (256 on gfx950), each walking its tiles
+  constexpr int kComputeUnits = 256;
+  auto kern = rowwise ? (kfull ? k_gemm_fp8_pers<true, true, F32, FA, ACC>
+                               : k_gemm_fp8_pers<false, true, F32, FA, ACC>)
+                      : (kfull ? k_gemm_fp8_pers<true, false, F32, FA, ACC>
+                               : k_gemm_fp8_pers<false, false, F32, FA, ACC>);
+  const int grid = blocks < kComputeUnits ? blocks : kComputeUnits;
+#else
   auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true, F32, FA, ACC>
                                : k_gemm_fp8_tn<false, true, F32, FA, ACC>)
                       : (kfull ? k_gemm_fp8_tn<true, false, F32, FA, ACC>
                                : k_gemm_fp8_tn<false, false, F32, FA, ACC>);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(THREADS), 0, stream, g);
+  const int grid = blocks;
+#endif
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(THREADS), 0, stream, g);
   return hipGetLastError();
 }
 
