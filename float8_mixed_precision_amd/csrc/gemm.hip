@@ -75,6 +75,7 @@
 // more than rounding order where a group holds products 14 or more binades
 // apart; the parity tests bound that difference per element.
 #include "fp8l_internal.h"
+#include "gemm_schedule.h"
 
 // 1: the persistent kernel (k_gemm_fp8_pers), 0: one workgroup per tile
 #ifndef FP8L_GEMM_PERSISTENT
@@ -195,7 +196,18 @@ struct GemmGroup {
   int tiles_m[MAX_GROUP], tiles_n[MAX_GROUP], first[MAX_GROUP];
   int count;
   int total;   // tiles of all problems
+  // persistent kernel: nonzero when the two arrays below hold a balanced
+  // schedule (gemm_schedule.h): the entry of workgroup l of XCD x for
+  // problem p in half l % 2 of sched[x][p][l / 2], the smallest count of XCD
+  // x's workgroups for problem p in byte p of sched_min[x] (whole words, so
+  // that the kernel reads them with scalar loads)
+  int balanced;
+  uint32_t sched_min[NUM_XCD];
+  uint32_t sched[NUM_XCD][MAX_GROUP][16];
 };
+static_assert(NUM_XCD == sched::XCDS && MAX_GROUP == sched::MAX_PROBLEMS &&
+              sched::MAX_WG == 32, "schedule layout");
+static_assert(sizeof(GemmGroup) <= 4096, "kernel arguments");
 
 // element i of a kernel-argument array for a wave-uniform i (selects, so the
 // array is never copied to private memory)
@@ -662,36 +674,65 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// This lane's index in its wave (0..63), read from the hardware at the
+// point of use (v_mbcnt over a full mask).  Volatile, so the compiler
+// neither keeps an earlier copy live across the loops (nor spills one) to
+// reuse here: it recomputes it in two instructions.
+__device__ __forceinline__ int hw_lane() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
+
 // Tile i (i = 0, 1, ...) of persistent workgroup b.  Workgroups are dealt
-// to the XCDs round-robin (b on XCD b % 8), and each XCD works through its
-// own contiguous share of every problem's grouped tile order, problem after
-// problem, as the XCD's blocks would with one workgroup per tile
-// (tile_of_block): its nx workgroups take positions l, l + nx, l + 2 nx, ...
-// (l = b / 8) of that sequence, so the tiles an XCD runs at one time are
-// neighbours in the grouped order and share operand panels in its L2.
+// to the XCDs round-robin (b on XCD x = b % 8, the l-th of its nx, l =
+// b / 8), and each XCD works through its own contiguous share of every
+// problem's grouped tile order, problem after problem, as the XCD's blocks
+// would with one workgroup per tile (tile_of_block).  Without a schedule the
+// XCD's workgroups take positions l, l + nx, l + 2 nx, ... of that sequence;
+// with one (g.balanced) workgroup l runs the count of tiles of problem p
+// that its entry gives, at the positions sched::position assigns.  Either
+// way the tiles an
+// XCD runs at one time are neighbours in the grouped order and share operand
+// panels in its L2.
 struct TileCoord {
   int pi, m0, n0;
   bool valid;
 };
 __device__ __forceinline__ TileCoord decode_tile(const GemmGroup &g, int b, int i, int G) {
   const int x = b % NUM_XCD;
+  const int l = b / NUM_XCD;
   const int nx = (G - x + NUM_XCD - 1) / NUM_XCD;   // workgroups on XCD x
-  int s = b / NUM_XCD + i * nx;                      // position in XCD x's sequence
+  int s = l + i * nx;                                // round-robin position
   for (int pi = 0; pi < g.count; ++pi) {
     const int tiles_m = pick(g.tiles_m, pi), tiles_n = pick(g.tiles_n, pi);
     const int T = tiles_m * tiles_n;
-    const int cnt = (T - x + NUM_XCD - 1) / NUM_XCD;  // XCD x's share of problem pi
-    if (s < cnt) {
-      int base = 0;
-      for (int xx = 0; xx < x; ++xx) base += (T - xx + NUM_XCD - 1) / NUM_XCD;
-      const int q = base + s;                        // grouped order index
-      const int group = GROUP_M * tiles_n;
-      const int first_m = (q / group) * GROUP_M;
-      const int gm = min(tiles_m - first_m, GROUP_M);
-      const int in_group = q % group;
-      return {pi, (first_m + in_group % gm) * BM, (in_group / gm) * BN, true};
+    int pos;                                         // position in XCD x's share
+    if (g.balanced) {
+      const uint32_t e = g.sched[x][pi][l >> 1] >> (16 * (l & 1));
+      const int n = (int)(e & 255);
+      if (i >= n) {
+        i -= n;
+        continue;
+      }
+      pos = sched::position(i, l, nx, (int)((g.sched_min[x] >> (8 * pi)) & 255),
+                            (int)((e >> 8) & 255));
+    } else {
+      const int cnt = (T - x + NUM_XCD - 1) / NUM_XCD;  // XCD x's share of problem pi
+      if (s >= cnt) {
+        s -= cnt;
+        continue;
+      }
+      pos = s;
     }
-    s -= cnt;
+    int base = 0;
+    for (int xx = 0; xx < x; ++xx) base += (T - xx + NUM_XCD - 1) / NUM_XCD;
+    const int q = base + pos;                          // grouped order index
+    const int group = GROUP_M * tiles_n;
+    const int first_m = (q / group) * GROUP_M;
+    const int gm = min(tiles_m - first_m, GROUP_M);
+    const int in_group = q % group;
+    return {pi, (first_m + in_group % gm) * BM, (in_group / gm) * BN, true};
   }
   return {0, 0, 0, false};
 }
@@ -720,50 +761,80 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
   const int c_odd = c_even ^ 1;
   int d_tile = 0, d_kt = 0, d_nk = 0, d_K = -1;     // d_tile: this workgroup's tile index
   bool d_valid = true;
+  // Tile coordinates, decoded once per tile at its top instead of inside the
+  // main loop: a_*, b_*, c_* are this workgroup's tiles cur, cur + 1 and
+  // cur + 2 (problem, first row and column, and whether the tile exists).
+  // The cursor runs at most two units ahead of the MFMAs, so while tile i
+  // computes (cur = i + 1 once its top has passed) it reaches at most tile
+  // i + 2; before the first tile it reaches at most tile 2.
+  int a_pi, a_m0, a_n0, b_pi, b_m0, b_n0, c_pi, c_m0, c_n0;
+  bool a_ok, b_ok, c_ok;
+  {
+    const TileCoord t0 = decode_tile(g, blockIdx.x, 0, G);
+    const TileCoord t1 = decode_tile(g, blockIdx.x, 1, G);
+    const TileCoord t2 = decode_tile(g, blockIdx.x, 2, G);
+    a_pi = t0.pi; a_m0 = t0.m0; a_n0 = t0.n0; a_ok = t0.valid;
+    b_pi = t1.pi; b_m0 = t1.m0; b_n0 = t1.n0; b_ok = t1.valid;
+    c_pi = t2.pi; c_m0 = t2.m0; c_n0 = t2.n0; c_ok = t2.valid;
+  }
+  int cur = 0;
   __amdgpu_buffer_rsrc_t d_rsA, d_rsB;
   uint32_t voff[16];
-  // per-lane offsets for the cursor's K, from an opaque copy of the lane
-  // index (recomputed where needed rather than kept live or spilled)
-  auto set_voff = [&]() {
-    int lane_v = lane;
-    asm volatile("" : "+v"(lane_v));
-    const int lr_v = lane_v >> 3;
-    const int ce_v = (lane_v & 7) ^ lr_v;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = wave * 64 + (q & 7) * 8 + lr_v;
-      voff[q] = (uint32_t)(row * d_K + ((q & 1) ? ce_v ^ 1 : ce_v) * 16);
-    }
-  };
-  auto d_setup = [&]() {
-    TileCoord tc = decode_tile(g, blockIdx.x, d_tile, G);
-    d_valid = tc.valid;
-    if (!d_valid) tc = decode_tile(g, 0, 0, G);
-    const int M = pick(g.M, tc.pi), N = pick(g.N, tc.pi);
-    const int K = pick(g.K, tc.pi);
-    d_nk = (K + BK - 1) / BK;
-    // an exhausted cursor still issues its (zero-filling) transfers into
-    // the stage no one reads any more: an empty buffer
-    d_rsA = __builtin_amdgcn_make_buffer_rsrc((void *)(pick(g.A, tc.pi) + (size_t)tc.m0 * K),
-                                              (short)0, d_valid ? (M - tc.m0) * K : 0,
-                                              0x00020000);
-    d_rsB = __builtin_amdgcn_make_buffer_rsrc((void *)(pick(g.B, tc.pi) + (size_t)tc.n0 * K),
-                                              (short)0, d_valid ? (N - tc.n0) * K : 0,
-                                              0x00020000);
-    if (K != d_K) {
-      d_K = K;
-      set_voff();
-    }
-  };
-  auto d_advance = [&]() {
-    if (!d_valid) return;
-    if (++d_kt == d_nk) {
-      d_kt = 0;
-      ++d_tile;
-      d_setup();
-    }
-  };
-  d_setup();
+  // The cursor's steps are macros rather than lambdas: a lambda reaches the
+  // kernel's variables through its captured references, and once inlined a
+  // choice between two of them can turn into a load through a chosen
+  // pointer, which pins the variables (and a copy of the kernel arguments)
+  // in private memory.
+  //
+  // FP8P_SETVOFF: per-lane offsets for the cursor's K, from the lane index
+  // read afresh (recomputed where needed rather than kept live or spilled).
+#define FP8P_SETVOFF()                                                          \
+  do {                                                                          \
+    const int lane_v = hw_lane();                                               \
+    const int lr_v = lane_v >> 3;                                               \
+    const int ce_v = (lane_v & 7) ^ lr_v;                                       \
+    _Pragma("unroll") for (int q = 0; q < 16; ++q) {                            \
+      const int row = wave * 64 + (q & 7) * 8 + lr_v;                           \
+      voff[q] = (uint32_t)(row * d_K + ((q & 1) ? ce_v ^ 1 : ce_v) * 16);       \
+    }                                                                           \
+  } while (0)
+  // FP8P_DSETUP: the cursor enters tile d_tile.  The host orders a launch's
+  // problems by decreasing K, so a tile with K = 0 is followed by no tile
+  // that needs operands: the cursor stops there.  Past the last tile
+  // decode_tile gives problem 0's origin, which serves the empty buffers
+  // an exhausted cursor still issues its (zero-filling) transfers from, into
+  // the stage no one reads any more.
+#define FP8P_DSETUP()                                                           \
+  do {                                                                          \
+    const bool sa_ = d_tile == cur, sb_ = d_tile == cur + 1;                    \
+    const int pi_ = sa_ ? a_pi : (sb_ ? b_pi : c_pi);                           \
+    const int m0_ = sa_ ? a_m0 : (sb_ ? b_m0 : c_m0);                           \
+    const int n0_ = sa_ ? a_n0 : (sb_ ? b_n0 : c_n0);                           \
+    const bool ok_ = sa_ ? a_ok : (sb_ ? b_ok : c_ok);                          \
+    const int M_ = pick(g.M, pi_), N_ = pick(g.N, pi_), K_ = pick(g.K, pi_);    \
+    d_nk = (K_ + BK - 1) / BK;                                                  \
+    d_valid = ok_ && d_nk > 0;                                                  \
+    d_rsA = __builtin_amdgcn_make_buffer_rsrc(                                  \
+        (void *)(pick(g.A, pi_) + (size_t)m0_ * K_), (short)0,                  \
+        d_valid ? (M_ - m0_) * K_ : 0, 0x00020000);                             \
+    d_rsB = __builtin_amdgcn_make_buffer_rsrc(                                  \
+        (void *)(pick(g.B, pi_) + (size_t)n0_ * K_), (short)0,                  \
+        d_valid ? (N_ - n0_) * K_ : 0, 0x00020000);                             \
+    if (K_ != d_K) {                                                            \
+      d_K = K_;                                                                 \
+      FP8P_SETVOFF();                                                           \
+    }                                                                           \
+  } while (0)
+  // FP8P_DADV: the cursor moves to the next unit
+#define FP8P_DADV()                                                             \
+  do {                                                                          \
+    if (d_valid && ++d_kt == d_nk) {                                            \
+      d_kt = 0;                                                                 \
+      ++d_tile;                                                                 \
+      FP8P_DSETUP();                                                            \
+    }                                                                           \
+  } while (0)
+  FP8P_DSETUP();
 
 #define FP8P_DMA1(STAGE, Q)                                                       \
   do {                                                                            \
@@ -874,10 +945,10 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
   if (d_valid) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) FP8P_DMA1(0, q);
-    d_advance();
+    FP8P_DADV();
 #pragma unroll
     for (int q = 0; q < 16; ++q) FP8P_DMA1(1, q);
-    d_advance();
+    FP8P_DADV();
   }
   wait_vmcnt0();
   barrier_lds();
@@ -892,7 +963,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 #pragma unroll
     for (int i = 0; i < NF; ++i) acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};
   for (int tile = 0;; ++tile) {
-    const TileCoord tc = decode_tile(g, blockIdx.x, tile, G);
+    const TileCoord tc = {a_pi, a_m0, a_n0, a_ok};
     if (!tc.valid) break;
     const int pi = tc.pi, m0 = tc.m0, n0 = tc.n0;
     const int M = pick(g.M, pi), N = pick(g.N, pi), K = pick(g.K, pi);
@@ -908,16 +979,17 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     // (free since the previous tile's closing barrier; read after the next
     // barrier)
     if (RW) {
+      const int t = wave * 64 + hw_lane();
       float *w = reinterpret_cast<float *>(lds + EPI_OFF);
-      w[tid] = m0 + tid < M ? 1.0f / sa[m0 + tid] : 0.f;
-      w[BM + tid] = n0 + tid < N ? 1.0f / sb[n0 + tid] : 0.f;
+      w[t] = m0 + t < M ? 1.0f / sa[m0 + t] : 0.f;
+      w[BM + t] = n0 + t < N ? 1.0f / sb[n0 + t] : 0.f;
     }
-    // the cursor's per-lane offsets, recomputed here from an opaque copy of
-    // the lane index instead of being kept (or spilled) across the epilogue
-    set_voff();
+    // the cursor's per-lane offsets and the fragment offsets, recomputed
+    // here from the lane index instead of being kept (or spilled) across the
+    // epilogue
+    FP8P_SETVOFF();
     {
-      int lane_v = lane;
-      asm volatile("" : "+v"(lane_v));
+      const int lane_v = hw_lane();
       // fragment f of A: rows wm*128 + f*16 + lane%16; lane reads logical
       // chunks 2(lane/16) and 2(lane/16)+1, swizzled by h(row)
       const int hr = (lane_v & 7) ^ ((lane_v >> 3) & 1);
@@ -934,6 +1006,16 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       for (int f = 0; f < 4; ++f) { FP8P_RD(st, 0, f, 0); FP8P_RD(st, 0, f, 1); }
 #pragma unroll
       for (int f = 0; f < 7; ++f) { FP8P_RD(st, 1, f, 0); FP8P_RD(st, 1, f, 1); }
+    }
+    // the decoded tiles move on while those reads are in flight
+    a_pi = b_pi; a_m0 = b_m0; a_n0 = b_n0; a_ok = b_ok;
+    b_pi = c_pi; b_m0 = c_m0; b_n0 = c_n0; b_ok = c_ok;
+    {
+      const TileCoord t3 = decode_tile(g, blockIdx.x, tile + 3, G);
+      c_pi = t3.pi; c_m0 = t3.m0; c_n0 = t3.n0; c_ok = t3.valid;
+    }
+    ++cur;
+    if (nk > 0) {
       // the accumulators hold zeros here: cleared before the first tile and
       // by the previous tile's epilogue as it read them (one definition
       // reaches the loop, so every accumulator block stays in its AGPRs)
@@ -950,7 +1032,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
         wait_lgkm0();
         barrier_lds();
         FP8P_H2(st ^ 1, st)
-        d_advance();
+        FP8P_DADV();
         st ^= 1;
 #ifdef FP8L_PHASE_TIMING
         if (t == 0) {
@@ -967,7 +1049,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       wait_lgkm0();
       barrier_lds();
       FP8P_H2D(st)
-      d_advance();
+      FP8P_DADV();
       st ^= 1;
     } else {
       if (RW) barrier_lds();                      // the inverse scales are written
@@ -982,9 +1064,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     // write whole rows
     const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
         pick(g.C, pi), (short)0, M * N * (F32 ? 4 : 2), 0x00020000);
-    int tid_e = tid;
-    asm volatile("" : "+v"(tid_e));
-    const int lane_e = tid_e & 63;
+    const int lane_e = hw_lane();
     const int ml16 = lane_e & 15;                 // row within a 16-row block
     const int nq = (lane_e >> 4) * 4;             // first of the lane's 4 columns in a block
     const float inv_a0 = RW ? 0.f : 1.0f / sa[0];
@@ -1080,7 +1160,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     }
 #ifdef FP8L_PHASE_TIMING
     const int slot = tile * G + (int)blockIdx.x;    // round-major record index
-    if (tid == 0 && slot < PHASE_MAX_BLOCKS) {
+    if (wave == 0 && hw_lane() == 0 && slot < PHASE_MAX_BLOCKS) {
       const unsigned long long ph_t2 = __builtin_amdgcn_s_memtime();
       const unsigned long long ph_r2 = __builtin_amdgcn_s_memrealtime();
       unsigned long long *d = g_phase + (size_t)slot * 8;
@@ -1101,6 +1181,9 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 #undef FP8P_MF
 #undef FP8P_RD
 #undef FP8P_DMA1
+#undef FP8P_DADV
+#undef FP8P_DSETUP
+#undef FP8P_SETVOFF
 }
 
 }  // namespace
@@ -1114,8 +1197,21 @@ hipError_t launch_group(const GemmDesc *d, int count, int rowwise, hipStream_t s
   GemmGroup g = {};
   int blocks = 0;
   bool kfull = true;
-  for (int i = 0; i < count; ++i) {
-    if (d[i].M == 0 || d[i].N == 0) continue;
+  // the problems in launch order: longest K first (stable), so that a
+  // balanced schedule places the long tiles first
+  int order[MAX_GROUP], n_order = 0;
+  for (int i = 0; i < count; ++i)
+    if (d[i].M != 0 && d[i].N != 0) order[n_order++] = i;
+#if FP8L_GEMM_PERSISTENT
+  for (int a = 1; a < n_order; ++a)
+    for (int b = a; b > 0 && d[order[b]].K > d[order[b - 1]].K; --b) {
+      const int t = order[b];
+      order[b] = order[b - 1];
+      order[b - 1] = t;
+    }
+#endif
+  for (int o = 0; o < n_order; ++o) {
+    const int i = order[o];
     const int c = g.count++;
     g.A[c] = d[i].A;
     g.sa[c] = d[i].sa;
@@ -1141,6 +1237,26 @@ hipError_t launch_group(const GemmDesc *d, int count, int rowwise, hipStream_t s
                       : (kfull ? k_gemm_fp8_pers<true, false, F32, FA, ACC>
                                : k_gemm_fp8_pers<false, false, F32, FA, ACC>);
   const int grid = blocks < kComputeUnits ? blocks : kComputeUnits;
+  // equal K: round-robin dealing is already the balanced schedule
+  bool mixed = false;
+  for (int c = 1; c < g.count; ++c) mixed = mixed || g.K[c] != g.K[0];
+  if (mixed) {
+    int tiles[MAX_GROUP], ktiles[MAX_GROUP];
+    for (int c = 0; c < g.count; ++c) {
+      tiles[c] = g.tiles_m[c] * g.tiles_n[c];
+      ktiles[c] = (g.K[c] + BK - 1) / BK;
+    }
+    sched::Packed pk;
+    if (sched::balance(grid, g.count, tiles, ktiles, pk)) {
+      g.balanced = 1;
+      for (int x = 0; x < NUM_XCD; ++x)
+        for (int c = 0; c < MAX_GROUP; ++c) {
+          g.sched_min[x] |= (uint32_t)pk.min_count[x][c] << (8 * c);
+          for (int l = 0; l < 32; ++l)
+            g.sched[x][c][l >> 1] |= (uint32_t)pk.entry[x][c][l] << (16 * (l & 1));
+        }
+    }
+  }
 #else
   auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true, F32, FA, ACC>
                                : k_gemm_fp8_tn<false, true, F32, FA, ACC>)

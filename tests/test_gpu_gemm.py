@@ -150,6 +150,41 @@ def test_gemm_grouped(rowwise, e5m2):
         assert torch.equal(f, single[2])
 
 
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+def test_gemm_grouped_mixed_k(rowwise):
+    """A grouped launch whose problems have different K, the first with K = 0
+    (an all-zero output) and the rest given in increasing K: every output
+    equals its own launch bit for bit, and the longest is checked against
+    the oracle."""
+    shapes = [(96, 80, 0), (272, 400, 208), (304, 256, 1024), (528, 272, 2048)]
+    ops_in, outs = [], []
+    for i, (m, n, k) in enumerate(shapes):
+        if k == 0:
+            qa = (np.zeros((m, 0), np.uint8), np.ones(m if rowwise else 1, np.float32))
+            qb = (np.zeros((n, 0), np.uint8), np.ones(n if rowwise else 1, np.float32))
+            ops_in.append((qa[0], qa[1], qb[0], qb[1]))
+        else:
+            qa = oracle.quantize(W.random_bf16(90 + i, (m, k), 1.0, 0), rowwise)
+            qb = oracle.quantize(W.random_bf16(90 + i, (n, k), 0.02, 1), rowwise)
+            ops_in.append((qa[0], qa[2], qb[0], qb[2]))
+        outs.append(torch.full((m, n), 3.0, dtype=torch.bfloat16, device=G.DEV))
+    dev = [(G.dev_u8(a), G.dev_f32(sa), G.dev_u8(b), G.dev_f32(sb)) for a, sa, b, sb in ops_in]
+    G.say("gemm grouped mixed K", shapes, "rowwise", rowwise)
+    ops.fp8_linear_gemm_grouped([d + (o,) for d, o in zip(dev, outs)], rowwise)
+    single = []
+    for (a, sa, b, sb), (m, n, k) in zip(dev, shapes):
+        o = torch.full((m, n), 5.0, dtype=torch.bfloat16, device=G.DEV)
+        ops.fp8_linear_gemm_grouped([(a, sa, b, sb, o)], rowwise)
+        single.append(o)
+    torch.cuda.synchronize()
+    assert torch.all(outs[0] == 0)
+    for i, (g, s1) in enumerate(zip(outs, single)):
+        assert torch.equal(g, s1), "problem %d differs from its own launch" % i
+    a, sa, b, sb = ops_in[3]
+    want = oracle.gemm_tn(a, sa, b, sb)
+    G.gemm_parity(G.host(outs[3]), want, a, b, sa, sb, label="mixed K [3]")
+
+
 def _sampled_parity_at(a, sa, b, sb, out, rows, cols, label):
     """The oracle's values at rows x cols (every pair) against out's."""
     ii, jj = (np.repeat(rows, len(cols)), np.tile(cols, len(rows)))
