@@ -32,7 +32,8 @@ if ROOT not in sys.path:
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
-GEMM_SOURCE = os.path.join(ROOT, "float8_mixed_precision_amd", "csrc", "gemm.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "float8_mixed_precision_amd", "csrc", f)
+                for f in ("gemm.hip", "gemm_schedule.h")]
 
 
 def parse():
@@ -73,8 +74,12 @@ def copy_calibration(nbytes: int):
 
 
 def gemm_source_hash() -> str:
-    with open(GEMM_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the GEMM's sources (the kernel and its host-side schedule)."""
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -858,7 +863,7 @@ def main():
                    "flops_per_step": wl.flops},
         "pct_fp8_peak_step": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "roofline": {
-            "kernel": "k_gemm_fp8_tn (each linear's fwd, grad_x and grad_w in one grouped "
+            "kernel": "k_gemm_fp8_pers (each linear's fwd, grad_x and grad_w in one grouped "
                       "launch; w1's grad_w in w3's)",
             "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),

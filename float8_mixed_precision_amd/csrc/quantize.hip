@@ -384,13 +384,18 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
       t[4 + k] = ((hi[0] >> sh) & 0xFFu) | (((hi[1] >> sh) & 0xFFu) << 8) |
                  (((hi[2] >> sh) & 0xFFu) << 16) | (((hi[3] >> sh) & 0xFFu) << 24);
     }
+    // Column col's 128 codes sit in one 128-byte LDS row: 16-row chunk
+    // ch at ch ^ (col / 8 % 8), and within it the 4-row dword s at
+    // s ^ 2 (col / 64).  A half-wave's writes (c8 = 0..15, two row groups)
+    // then hit 32 distinct banks: the chunk swizzle separates c8 % 8, the
+    // dword swap c8 and c8 + 8.
     const int chunk = rl >> 4;                // 16-row chunk of the column
     const int pchunk = chunk ^ (c8 & 7);
-    const int inner = rl & 15;
+    const int slot = ((rl >> 2) & 3) ^ ((c8 >> 3) << 1);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int col = c8 * 8 + k;
-      *reinterpret_cast<uint32_t *>(lds + col * CT_T + pchunk * 16 + inner) = t[k];
+      *reinterpret_cast<uint32_t *>(lds + col * CT_T + pchunk * 16 + slot * 4) = t[k];
     }
   }
   __syncthreads();
@@ -404,7 +409,8 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
     const int gr = r0 + rc * 16;
     if (gc < cols && gr < rows) {
       const int pc = rc ^ ((col >> 3) & 7);
-      const v4u_t v = *reinterpret_cast<const v4u_t *>(lds + col * CT_T + pc * 16);
+      v4u_t v = *reinterpret_cast<const v4u_t *>(lds + col * CT_T + pc * 16);
+      if (col & 64) v = (v4u_t){v.z, v.w, v.x, v.y};   // undo the dword swap
       v4u_t *tdst = reinterpret_cast<v4u_t *>(qt + (size_t)gc * rows + gr);
       if (CT_NT)
         __builtin_nontemporal_store(v, tdst);
