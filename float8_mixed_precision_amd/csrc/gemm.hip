@@ -1060,8 +1060,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 #endif
 
     // ---- epilogue: scale, round, stage 32 rows of the wave's 128 x 128 tile
-    // at a time in the wave's 8 KB (row r's 16-byte chunk c at c ^ (r % 16)),
-    // write whole rows
+    // at a time in the wave's 8 KB (row r's 16-byte chunk c at c ^ (r % 16),
+    // its 8-byte halves swapped where r % 16 >= 8), write whole rows
     const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
         pick(g.C, pi), (short)0, M * N * (F32 ? 4 : 2), 0x00020000);
     const int lane_e = hw_lane();
@@ -1122,9 +1122,12 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
             acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};  // cleared for the next tile
             const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
             const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
-            // byte column (j*16 + nq)*2: chunk 2j + nq/8, 8 bytes in at (nq%8)*2
+            // byte column (j*16 + nq)*2: chunk 2j + nq/8, 8 bytes in at
+            // (nq%8)*2, the two halves of the chunk swapped in rows 8..15 of
+            // a block (16 lanes of one write then cover all 32 banks)
             const int ch = (2 * j + (nq >> 3)) ^ ml16;
-            *reinterpret_cast<uint2 *>(epi + ml * 256 + ch * 16 + (nq & 7) * 2) =
+            *reinterpret_cast<uint2 *>(epi + ml * 256 + ch * 16 +
+                                       (((nq & 7) * 2) ^ ((ml16 >> 3) << 3))) =
                 make_uint2(p01, p23);
           }
         }
@@ -1136,6 +1139,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
         for (int u = 0; u < 8; ++u) {
           const int r = u * 4 + (lane_e >> 4);
           v[u] = *reinterpret_cast<const v4u *>(epi + r * 256 + (((lane_e & 15) ^ (r & 15)) * 16));
+          // rows with r % 16 >= 8 (u = 2, 3, 6, 7) hold their halves swapped
+          if (u & 2) v[u] = (v4u){v[u].z, v[u].w, v[u].x, v[u].y};
           const bool ok = col_ok && srow + u * 4 < M;
           off[u] = ok ? (uint32_t)(((srow + u * 4) * N + scol) * 2) : OOB_C;
         }
