@@ -699,13 +699,15 @@ def measure_board(run_step, seconds: float = 2.5):
 
 
 def phase_timing():
-    """Per-workgroup phases of the GEMM (libfp8phase.so: the same kernels
-    with shader-clock and 100 MHz real-time counters read at a workgroup's
-    start, after its prologue, after its main loop and after its last store)
-    for the forward, grad_X and grad_W shapes of the 8B FFN's w1, each
-    launched back to back on E4M3 codes of N(0,1) activations and N(0,0.02)
-    weights quantized by this library.  Medians over the workgroups of the
-    last launch; the clock is shader cycles over real time."""
+    """Per-tile phases of the persistent GEMM (libfp8phase.so: the same
+    kernels with shader-clock and 100 MHz real-time counters read at a
+    tile's top, after its first k-tile, after its last k-tile and after its
+    last store is issued) for the forward, grad_X and grad_W shapes of the
+    8B FFN's w1, each launched back to back on E4M3 codes of N(0,1)
+    activations and N(0,0.02) weights quantized by this library.  Medians
+    over the tiles of the last launch; the gap is from a tile's last store to
+    the top of the same workgroup's next tile, the period from one tile's top
+    to the next's; the clock is shader cycles over real time."""
     import ctypes
     import numpy as np
     import torch
@@ -744,20 +746,22 @@ def phase_timing():
         d = buf.reshape(nb, 8).astype(np.int64)
         t0, r0, ta, ra, t1, r1, t2, r2 = (d[:, i] for i in range(8))
         nk = K // 128
+        G = min(nb, 256)                  # workgroups; record s + G is the next tile of s's
         clk = (t2 - t0) / ((r2 - r0) / 100e6) / 1e9
         loop = float(np.median(t1 - ta))
-        tile = float(np.median(t2 - t0))
-        out.append({"gemm": name, "M_N_K": [M, N, K], "workgroups": nb,
+        period = float(np.median(t0[G:] - t0[:-G]))
+        out.append({"gemm": name, "M_N_K": [M, N, K], "tiles": nb, "workgroups": G,
                     "avg_launch_us": round(us, 1),
                     "tflops": round(2 * M * N * K / us / 1e6, 1),
                     "clock_ghz_median": round(float(np.median(clk)), 3),
                     "clock_ghz_min_max": [round(float(clk.min()), 3), round(float(clk.max()), 3)],
-                    "prologue_cycles": int(np.median(ta - t0)),
-                    "loop_cycles_per_ktile": round(loop / nk, 1),
-                    "loop_issue_efficiency": round(2048 * nk / loop, 4),
+                    "head_cycles": int(np.median(ta - t0)),
+                    "loop_cycles_per_ktile": round(loop / (nk - 1), 1),
+                    "loop_issue_efficiency": round(2048 * (nk - 1) / loop, 4),
                     "epilogue_cycles": int(np.median(t2 - t1)),
-                    "tile_cycles": int(tile),
-                    "mfma_share_of_tile": round(2048 * nk / tile, 4)})
+                    "gap_cycles": int(np.median(t0[G:] - t2[:-G])),
+                    "tile_period_cycles": int(period),
+                    "mfma_share_of_period": round(2048 * nk / period, 4)})
         del a, b, qa, qb, o
     print(json.dumps({"phase_timing": out}), flush=True)
 

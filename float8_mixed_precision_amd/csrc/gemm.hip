@@ -966,6 +966,16 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     const TileCoord tc = {a_pi, a_m0, a_n0, a_ok};
     if (!tc.valid) break;
     const int pi = tc.pi, m0 = tc.m0, n0 = tc.n0;
+    // the decoded tiles move on, before the fragment reads below: the
+    // decode's scalar loads share the LDS reads' wait counter, and waiting
+    // for them here waits for nothing else
+    a_pi = b_pi; a_m0 = b_m0; a_n0 = b_n0; a_ok = b_ok;
+    b_pi = c_pi; b_m0 = c_m0; b_n0 = c_n0; b_ok = c_ok;
+    {
+      const TileCoord t3 = decode_tile(g, blockIdx.x, tile + 3, G);
+      c_pi = t3.pi; c_m0 = t3.m0; c_n0 = t3.n0; c_ok = t3.valid;
+    }
+    ++cur;
     const int M = pick(g.M, pi), N = pick(g.N, pi), K = pick(g.K, pi);
     const int nk = (K + BK - 1) / BK;
     const float *__restrict__ sa = pick(g.sa, pi);
@@ -1007,14 +1017,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 #pragma unroll
       for (int f = 0; f < 7; ++f) { FP8P_RD(st, 1, f, 0); FP8P_RD(st, 1, f, 1); }
     }
-    // the decoded tiles move on while those reads are in flight
-    a_pi = b_pi; a_m0 = b_m0; a_n0 = b_n0; a_ok = b_ok;
-    b_pi = c_pi; b_m0 = c_m0; b_n0 = c_n0; b_ok = c_ok;
-    {
-      const TileCoord t3 = decode_tile(g, blockIdx.x, tile + 3, G);
-      c_pi = t3.pi; c_m0 = t3.m0; c_n0 = t3.n0; c_ok = t3.valid;
-    }
-    ++cur;
     if (nk > 0) {
       // the accumulators hold zeros here: cleared before the first tile and
       // by the previous tile's epilogue as it read them (one definition
