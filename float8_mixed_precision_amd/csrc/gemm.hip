@@ -1175,10 +1175,14 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       d[4] = ph_t1; d[5] = ph_r1; d[6] = ph_t2; d[7] = ph_r2;
     }
 #endif
-    // every wave is done with the epilogue region before the next tile's
-    // inverse scales overwrite it
-    wait_lgkm0();
-    barrier_lds();
+    // rowwise: every wave is done with the epilogue region before the next
+    // tile's inverse scales overwrite it.  Otherwise a wave stages only in
+    // its own part of that region, and the next tile's operands were made
+    // visible by the barrier of this tile's last k-tile: no barrier here.
+    if (RW) {
+      wait_lgkm0();
+      barrier_lds();
+    }
   }
 #undef FP8P_H2D
 #undef FP8P_H2
