@@ -56,15 +56,19 @@
 //    fragment: output register r of lane l is n = 4 (l / 16) + r, m = l % 16
 //    of its 16 x 16 block, so a lane holds 4 consecutive n of one m.  The
 //    epilogue scales, rounds to bf16 (v_cvt_pk_bf16_f32, round to nearest
-//    even) and stages the 128 x 128 tile in LDS to write whole 256-byte rows
-//    with 16-byte buffer stores (out-of-range stores are dropped by the
-//    buffer bounds check).
-//  - Workgroups are renumbered so that each XCD receives one contiguous
-//    range of a grouped tile order (GROUP_M = 4 tile-rows at a time): the
-//    32 tiles an XCD runs at once form a 4 x 8 block, and at the 8B FFN
-//    shapes an XCD's whole range stays within one 4-row group, so its A
-//    panels are reused from L2 across successive waves of tiles (measured
-//    ~3% faster than 8 x 4 blocks, ~3% faster than 2 x 16).
+//    even) and stages the 128 x 128 tile in LDS, 32 rows at a time, to write
+//    whole 256-byte rows with 16-byte buffer stores (out-of-range stores are
+//    dropped by the buffer bounds check).
+//  - Persistent: one workgroup per compute unit walks a fixed list of tiles,
+//    with the operand loads of the next tile overlapping the end of the
+//    current one (k_gemm_fp8_pers below).  Each XCD works through its own
+//    contiguous share of a grouped tile order (GROUP_M = 4 tile-rows at a
+//    time): the 32 tiles an XCD runs at once form a 4 x 8 block, and at the
+//    8B FFN shapes an XCD's whole share stays within one 4-row group, so its
+//    A panels are reused from L2 across successive rounds of tiles
+//    (measured ~3% faster than 8 x 4 blocks, ~3% faster than 2 x 16).  A
+//    grouped launch of problems with different K follows a balanced
+//    schedule computed on the host (gemm_schedule.h).
 //
 // Accumulation.  The instruction's products are exact, but one k-step of
 // 128 products is not an fp32 sum in some order: probes of the bare
@@ -77,19 +81,15 @@
 #include "fp8l_internal.h"
 #include "gemm_schedule.h"
 
-// 1: the persistent kernel (k_gemm_fp8_pers), 0: one workgroup per tile
-#ifndef FP8L_GEMM_PERSISTENT
-#define FP8L_GEMM_PERSISTENT 1
-#endif
-
 namespace fp8l {
 #ifdef FP8L_PHASE_TIMING
 // Measurement build only (a separate library compiled with
-// -DFP8L_PHASE_TIMING): per workgroup, the shader-clock counter (s_memtime)
-// and the 100 MHz real-time counter (s_memrealtime) at the kernel's start,
-// after the prologue, after the main loop and after the last store is
-// issued, written by thread 0 for the first PHASE_MAX_BLOCKS workgroups of
-// the latest launch.  Read with fp8_gemm_phase_read.
+// -DFP8L_PHASE_TIMING): per tile, the shader-clock counter (s_memtime) and
+// the 100 MHz real-time counter (s_memrealtime) at the tile's top, after its
+// first k-tile, after its last k-tile and after its last store is issued,
+// written by one lane of the workgroup that ran it; record tile * G + b for
+// workgroup b's tile-th tile (G workgroups), the first PHASE_MAX_BLOCKS
+// records of the latest launch.  Read with fp8_gemm_phase_read.
 constexpr int PHASE_MAX_BLOCKS = 8192;
 __device__ unsigned long long g_phase[PHASE_MAX_BLOCKS * 8];
 #endif
@@ -105,9 +105,6 @@ constexpr int FR = 16;                   // rows per fragment
 constexpr int NF = WM / FR;              // fragments per operand per wave (8)
 constexpr int SLAB = BM * BK;            // 32 KB
 constexpr int STAGE_BYTES = 2 * SLAB;    // 64 KB: A slab, then B slab
-constexpr int EP_STRIDE = 272;           // staged output row: 256 B + 16 B pad
-constexpr int EP_WAVE = WM * EP_STRIDE;  // staged output of one wave
-constexpr int INV_OFF = 2 * STAGE_BYTES > 4 * EP_WAVE ? 2 * STAGE_BYTES : 4 * EP_WAVE;
 constexpr int INV_BYTES = (BM + BN) * 4;  // rowwise: 1/sa of the tile's rows, 1/sb of its cols
 constexpr int GROUP_M = 4;
 constexpr int NUM_XCD = 8;
@@ -161,30 +158,9 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_ad
 }
 #pragma clang diagnostic pop
 
-// blockIdx -> (tile_m, tile_n): blocks are dealt to the XCDs round-robin, so
-// block b runs on XCD b % 8.  Renumber so that each XCD receives one
-// contiguous range of the grouped tile order.
-__device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m,
-                                              int tiles_n, int &tm, int &tn) {
-  const int xcd = b % NUM_XCD;
-  const int local = b / NUM_XCD;
-  int base = 0;
-  for (int x = 0; x < xcd; ++x) base += (nblocks - x + NUM_XCD - 1) / NUM_XCD;
-  const int p = base + local;
-  const int group = GROUP_M * tiles_n;
-  const int first_m = (p / group) * GROUP_M;
-  const int gm = min(tiles_m - first_m, GROUP_M);
-  const int in_group = p % group;
-  tm = first_m + in_group % gm;
-  tn = in_group / gm;
-}
-
-// Up to MAX_GROUP GEMMs of one variant in one launch: problem i owns the
-// workgroups [first[i], first[i] + tiles_m[i] * tiles_n[i]).  A grid whose
-// last round of tiles would leave CUs idle (896 tiles on 256 CUs) can share
-// that round with another problem.  first[i] is a multiple of 8 whenever
-// the problems before it have a multiple of 8 tiles, which keeps the XCD
-// mapping of tile_of_block.
+// Up to MAX_GROUP GEMMs of one variant in one launch (the kernel's only
+// argument).  A problem whose last round of tiles would leave compute units
+// idle (896 tiles on 256) shares that round with the others.
 constexpr int MAX_GROUP = 4;
 struct GemmGroup {
   const uint8_t *A[MAX_GROUP];
@@ -193,10 +169,10 @@ struct GemmGroup {
   const float *sb[MAX_GROUP];
   void *C[MAX_GROUP];
   int M[MAX_GROUP], N[MAX_GROUP], K[MAX_GROUP];
-  int tiles_m[MAX_GROUP], tiles_n[MAX_GROUP], first[MAX_GROUP];
+  int tiles_m[MAX_GROUP], tiles_n[MAX_GROUP];
   int count;
   int total;   // tiles of all problems
-  // persistent kernel: nonzero when the two arrays below hold a balanced
+  // nonzero when the two arrays below hold a balanced
   // schedule (gemm_schedule.h): the entry of workgroup l of XCD x for
   // problem p in half l % 2 of sched[x][p][l / 2], the smallest count of XCD
   // x's workgroups for problem p in byte p of sched_min[x] (whole words, so
@@ -218,430 +194,6 @@ __device__ __forceinline__ T pick(const T (&v)[MAX_GROUP], int i) {
   for (int k = 1; k < MAX_GROUP; ++k)
     if (i == k) r = v[k];
   return r;
-}
-
-// KFULL: K % 128 == 0 (no K tail, no per-chunk K check).  RW: rowwise
-// scales (sa[M], sb[N]) instead of one scale per operand.  F32: fp32 output
-// (the scaled value before bf16 rounding) instead of bf16.  FA: code format
-// of A (0 = E4M3, 1 = E5M2 gradients); B is E4M3.  The instruction's
-// format selectors apply to its first and second source operand, here the
-// B and the A fragment.  ACC (bf16 output only): C holds a bf16 matrix on
-// entry and receives bf16(fl32(C) + fl32(bf16 result)), the sum of two
-// gradient contributions as bf16 tensors add.
-template <bool KFULL, bool RW, bool F32, int FA, bool ACC>
-__global__ __launch_bounds__(THREADS) void k_gemm_fp8_tn(GemmGroup g) {
-  static_assert(!(F32 && ACC), "accumulation is into a bf16 output");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[INV_OFF + (RW ? INV_BYTES : 0)];
-
-  // this workgroup's problem (uniform) and its block index within it
-  int pi = 0;
-#pragma unroll
-  for (int i = 1; i < MAX_GROUP; ++i)
-    if (i < g.count && (int)blockIdx.x >= g.first[i]) pi = i;
-  const uint8_t *__restrict__ A = pick(g.A, pi);
-  const float *__restrict__ sa = pick(g.sa, pi);
-  const uint8_t *__restrict__ B = pick(g.B, pi);
-  const float *__restrict__ sb = pick(g.sb, pi);
-  void *__restrict__ C = pick(g.C, pi);
-  const int M = pick(g.M, pi), N = pick(g.N, pi), K = pick(g.K, pi);
-  const int tiles_m = pick(g.tiles_m, pi), tiles_n = pick(g.tiles_n, pi);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-
-  int tmi, tni;
-  tile_of_block((int)blockIdx.x - pick(g.first, pi), tiles_m * tiles_n, tiles_m, tiles_n, tmi,
-                tni);
-  const int m0 = tmi * BM;
-  const int n0 = tni * BN;
-#ifdef FP8L_PHASE_TIMING
-  const unsigned long long ph_t0 = __builtin_amdgcn_s_memtime();
-  const unsigned long long ph_r0 = __builtin_amdgcn_s_memrealtime();
-  unsigned long long ph_ta = ph_t0, ph_ra = ph_r0;
-#endif
-
-  // rowwise: the tile's 256 + 256 reciprocal scales, one of each per thread,
-  // into their own LDS region (read after the main loop's last barrier)
-  if (RW) {
-    float *inv = reinterpret_cast<float *>(lds + INV_OFF);
-    inv[tid] = m0 + tid < M ? 1.0f / sa[m0 + tid] : 0.f;
-    inv[BM + tid] = n0 + tid < N ? 1.0f / sb[n0 + tid] : 0.f;
-  }
-
-  const __amdgpu_buffer_rsrc_t rsA =
-      __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, M * K, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsB =
-      __builtin_amdgcn_make_buffer_rsrc((void *)B, (short)0, N * K, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsC =
-      __builtin_amdgcn_make_buffer_rsrc(C, (short)0, M * N * (F32 ? 4 : 2), 0x00020000);
-
-  // ---- DMA: wave w, instruction q (0..15; 0..7 A, 8..15 B) fills slab
-  // rows w*64 + (q&7)*8 + lane/8.  Row r keeps logical chunk c at physical
-  // chunk c ^ h(r) with h(r) = lane/8 ^ (q & 1) here, so lane i loads
-  // logical chunk (i % 8) ^ (i / 8) ^ (q & 1).  The per-lane row offsets are
-  // fixed for the whole loop; k0 travels in the scalar offset.
-  const int lr = lane >> 3;
-  const int c_even = (lane & 7) ^ lr;
-  const int c_odd = c_even ^ 1;
-  const int klim_e = K - c_even * 16;          // chunk valid while k0 < klim
-  const int klim_o = K - c_odd * 16;
-  uint32_t voff[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int row = (q >= 8 ? n0 : m0) + wave * 64 + (q & 7) * 8 + lr;
-    const int lim = q >= 8 ? N : M;
-    const int c = (q & 1) ? c_odd : c_even;
-    voff[q] = row < lim ? (uint32_t)(row * K + c * 16) : OOB;
-  }
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
-  const uint32_t wave_dst = lds_base + (uint32_t)(wave * 64 * BK);
-
-#define FP8L_DMA1(STAGE, KT, Q)                                                   \
-  do {                                                                            \
-    const uint32_t k0_ = (uint32_t)((KT) * BK);                                   \
-    const bool kok_ = KFULL || (int)k0_ < (((Q) & 1) ? klim_o : klim_e);          \
-    const uint32_t dst_ = wave_dst + (uint32_t)((STAGE) * STAGE_BYTES +           \
-                          ((Q) >= 8 ? SLAB : 0) + ((Q) & 7) * 1024);              \
-    dma16((Q) >= 8 ? rsB : rsA, dst_, kok_ ? voff[Q] : OOB, k0_);                 \
-  } while (0)
-
-  // ---- fragment reads: fragment f of A is rows wm*128 + f*16 + lane%16;
-  // lane l reads logical chunks 2(l/16) and 2(l/16)+1; h(row) depends only
-  // on lane%16
-  const int hr = (lane & 7) ^ ((lane >> 3) & 1);
-  const int g4 = lane >> 4;
-  const int fArow = (wm * WM + (lane & 15)) * BK;
-  const int fBrow = SLAB + (wn * WN + (lane & 15)) * BK;
-  const int fc0 = ((2 * g4) ^ hr) << 4;
-  const int fc1 = ((2 * g4 + 1) ^ hr) << 4;
-
-  v8i fa[NF], fb[NF];
-  v4f acc[NF][NF];   // [j: n block][i: m block]
-#pragma unroll
-  for (int j = 0; j < NF; ++j)
-#pragma unroll
-    for (int i = 0; i < NF; ++i) acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-  // half H (0: chunk 2(l/16), 1: the next) of fragment F of operand X
-#define FP8L_RD(STAGE, X, F, H)                                                   \
-  do {                                                                            \
-    const uint8_t *src_ = lds + (STAGE) * STAGE_BYTES +                           \
-                          ((X) ? fBrow : fArow) + (F) * FR * BK + ((H) ? fc1 : fc0); \
-    const v4u v_ = *reinterpret_cast<const v4u *>(src_);                          \
-    if (X) { fb[F][4 * (H)] = (int)v_.x; fb[F][4 * (H) + 1] = (int)v_.y;          \
-             fb[F][4 * (H) + 2] = (int)v_.z; fb[F][4 * (H) + 3] = (int)v_.w; }    \
-    else   { fa[F][4 * (H)] = (int)v_.x; fa[F][4 * (H) + 1] = (int)v_.y;          \
-             fa[F][4 * (H) + 2] = (int)v_.z; fa[F][4 * (H) + 3] = (int)v_.w; }    \
-  } while (0)
-#define FP8L_MF(J, I)                                                             \
-  acc[J][I] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                   \
-      fb[J], fa[I], acc[J][I], 0, FA, 0, 0, 0, 0)
-  // slot S (0..31) of a half runs MFMA (B frag S/4) x (A frag I0 + S%4 for
-  // odd S/4, I0 + 3 - S%4 for even S/4) plus the memory instructions listed
-  // for it; the A reads of each half come in the order of first use
-#define FP8L_M(S, I0) FP8L_MF((S) / 4, (I0) + ((((S) / 4) & 1) ? (S) % 4 : 3 - (S) % 4));
-#define FP8L_E() __builtin_amdgcn_sched_barrier(0);
-#define FP8L_H1(ST) \
-  FP8L_M(0, 0) FP8L_RD(ST, 0, 7, 0); FP8L_E() \
-  FP8L_M(1, 0) FP8L_RD(ST, 0, 7, 1); FP8L_E() \
-  FP8L_M(2, 0) FP8L_RD(ST, 0, 6, 0); FP8L_E() \
-  FP8L_M(3, 0) FP8L_RD(ST, 0, 6, 1); FP8L_E() \
-  FP8L_M(4, 0) FP8L_RD(ST, 0, 5, 0); FP8L_E() \
-  FP8L_M(5, 0) FP8L_RD(ST, 0, 5, 1); FP8L_E() \
-  FP8L_M(6, 0) FP8L_RD(ST, 0, 4, 0); FP8L_E() \
-  FP8L_M(7, 0) FP8L_RD(ST, 0, 4, 1); FP8L_E() \
-  FP8L_M(8, 0) FP8L_RD(ST, 1, 7, 0); FP8L_E() \
-  FP8L_M(9, 0) FP8L_RD(ST, 1, 7, 1); FP8L_E() \
-  FP8L_M(10, 0) FP8L_E() \
-  FP8L_M(11, 0) FP8L_E() \
-  FP8L_M(12, 0) FP8L_E() \
-  FP8L_M(13, 0) FP8L_E() \
-  FP8L_M(14, 0) FP8L_E() \
-  FP8L_M(15, 0) FP8L_E() \
-  FP8L_M(16, 0) FP8L_E() \
-  FP8L_M(17, 0) FP8L_E() \
-  FP8L_M(18, 0) FP8L_E() \
-  FP8L_M(19, 0) FP8L_E() \
-  FP8L_M(20, 0) FP8L_E() \
-  FP8L_M(21, 0) FP8L_E() \
-  FP8L_M(22, 0) FP8L_E() \
-  FP8L_M(23, 0) FP8L_E() \
-  FP8L_M(24, 0) FP8L_E() \
-  FP8L_M(25, 0) FP8L_E() \
-  FP8L_M(26, 0) FP8L_E() \
-  FP8L_M(27, 0) FP8L_E() \
-  FP8L_M(28, 0) FP8L_E() \
-  FP8L_M(29, 0) FP8L_E() \
-  FP8L_M(30, 0) FP8L_E() \
-  FP8L_M(31, 0) FP8L_E()
-#define FP8L_H2(STN, DST, KT) \
-  FP8L_M(0, 4) FP8L_RD(STN, 0, 3, 0); FP8L_E() \
-  FP8L_M(1, 4) FP8L_DMA1(DST, KT, 0); FP8L_E() \
-  FP8L_M(2, 4) FP8L_RD(STN, 0, 3, 1); FP8L_E() \
-  FP8L_M(3, 4) FP8L_DMA1(DST, KT, 1); FP8L_E() \
-  FP8L_M(4, 4) FP8L_RD(STN, 0, 2, 0); FP8L_RD(STN, 1, 0, 0); FP8L_E() \
-  FP8L_M(5, 4) FP8L_RD(STN, 1, 0, 1); FP8L_DMA1(DST, KT, 2); FP8L_E() \
-  FP8L_M(6, 4) FP8L_RD(STN, 0, 2, 1); FP8L_E() \
-  FP8L_M(7, 4) FP8L_DMA1(DST, KT, 3); FP8L_E() \
-  FP8L_M(8, 4) FP8L_RD(STN, 0, 1, 0); FP8L_RD(STN, 1, 1, 0); FP8L_E() \
-  FP8L_M(9, 4) FP8L_RD(STN, 1, 1, 1); FP8L_DMA1(DST, KT, 4); FP8L_E() \
-  FP8L_M(10, 4) FP8L_RD(STN, 0, 1, 1); FP8L_E() \
-  FP8L_M(11, 4) FP8L_DMA1(DST, KT, 5); FP8L_E() \
-  FP8L_M(12, 4) FP8L_RD(STN, 0, 0, 0); FP8L_RD(STN, 1, 2, 0); FP8L_E() \
-  FP8L_M(13, 4) FP8L_RD(STN, 1, 2, 1); FP8L_DMA1(DST, KT, 6); FP8L_E() \
-  FP8L_M(14, 4) FP8L_RD(STN, 0, 0, 1); FP8L_E() \
-  FP8L_M(15, 4) FP8L_DMA1(DST, KT, 7); FP8L_E() \
-  FP8L_M(16, 4) FP8L_RD(STN, 1, 3, 0); FP8L_E() \
-  FP8L_M(17, 4) FP8L_RD(STN, 1, 3, 1); FP8L_DMA1(DST, KT, 8); FP8L_E() \
-  FP8L_M(18, 4) FP8L_E() \
-  FP8L_M(19, 4) FP8L_DMA1(DST, KT, 9); FP8L_E() \
-  FP8L_M(20, 4) FP8L_RD(STN, 1, 4, 0); FP8L_E() \
-  FP8L_M(21, 4) FP8L_RD(STN, 1, 4, 1); FP8L_DMA1(DST, KT, 10); FP8L_E() \
-  FP8L_M(22, 4) FP8L_E() \
-  FP8L_M(23, 4) FP8L_DMA1(DST, KT, 11); FP8L_E() \
-  FP8L_M(24, 4) FP8L_RD(STN, 1, 5, 0); FP8L_E() \
-  FP8L_M(25, 4) FP8L_RD(STN, 1, 5, 1); FP8L_DMA1(DST, KT, 12); FP8L_E() \
-  FP8L_M(26, 4) FP8L_E() \
-  FP8L_M(27, 4) FP8L_DMA1(DST, KT, 13); FP8L_E() \
-  FP8L_M(28, 4) FP8L_RD(STN, 1, 6, 0); FP8L_E() \
-  FP8L_M(29, 4) FP8L_RD(STN, 1, 6, 1); FP8L_DMA1(DST, KT, 14); FP8L_E() \
-  FP8L_M(30, 4) FP8L_E() \
-  FP8L_M(31, 4) FP8L_DMA1(DST, KT, 15); FP8L_E()
-#define FP8L_H2N(STN) \
-  FP8L_M(0, 4) FP8L_RD(STN, 0, 3, 0); FP8L_E() \
-  FP8L_M(1, 4) FP8L_E() \
-  FP8L_M(2, 4) FP8L_RD(STN, 0, 3, 1); FP8L_E() \
-  FP8L_M(3, 4) FP8L_E() \
-  FP8L_M(4, 4) FP8L_RD(STN, 0, 2, 0); FP8L_RD(STN, 1, 0, 0); FP8L_E() \
-  FP8L_M(5, 4) FP8L_RD(STN, 1, 0, 1); FP8L_E() \
-  FP8L_M(6, 4) FP8L_RD(STN, 0, 2, 1); FP8L_E() \
-  FP8L_M(7, 4) FP8L_E() \
-  FP8L_M(8, 4) FP8L_RD(STN, 0, 1, 0); FP8L_RD(STN, 1, 1, 0); FP8L_E() \
-  FP8L_M(9, 4) FP8L_RD(STN, 1, 1, 1); FP8L_E() \
-  FP8L_M(10, 4) FP8L_RD(STN, 0, 1, 1); FP8L_E() \
-  FP8L_M(11, 4) FP8L_E() \
-  FP8L_M(12, 4) FP8L_RD(STN, 0, 0, 0); FP8L_RD(STN, 1, 2, 0); FP8L_E() \
-  FP8L_M(13, 4) FP8L_RD(STN, 1, 2, 1); FP8L_E() \
-  FP8L_M(14, 4) FP8L_RD(STN, 0, 0, 1); FP8L_E() \
-  FP8L_M(15, 4) FP8L_E() \
-  FP8L_M(16, 4) FP8L_RD(STN, 1, 3, 0); FP8L_E() \
-  FP8L_M(17, 4) FP8L_RD(STN, 1, 3, 1); FP8L_E() \
-  FP8L_M(18, 4) FP8L_E() \
-  FP8L_M(19, 4) FP8L_E() \
-  FP8L_M(20, 4) FP8L_RD(STN, 1, 4, 0); FP8L_E() \
-  FP8L_M(21, 4) FP8L_RD(STN, 1, 4, 1); FP8L_E() \
-  FP8L_M(22, 4) FP8L_E() \
-  FP8L_M(23, 4) FP8L_E() \
-  FP8L_M(24, 4) FP8L_RD(STN, 1, 5, 0); FP8L_E() \
-  FP8L_M(25, 4) FP8L_RD(STN, 1, 5, 1); FP8L_E() \
-  FP8L_M(26, 4) FP8L_E() \
-  FP8L_M(27, 4) FP8L_E() \
-  FP8L_M(28, 4) FP8L_RD(STN, 1, 6, 0); FP8L_E() \
-  FP8L_M(29, 4) FP8L_RD(STN, 1, 6, 1); FP8L_E() \
-  FP8L_M(30, 4) FP8L_E() \
-  FP8L_M(31, 4) FP8L_E()
-#define FP8L_SYNC()                                                               \
-  wait_vmcnt0();                                                                  \
-  wait_lgkm0();                                                                   \
-  barrier_lds();
-
-  const int nk = (K + BK - 1) / BK;
-  if (nk > 0) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) FP8L_DMA1(0, 0, q);
-    if (nk > 1) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) FP8L_DMA1(1, 1, q);
-    }
-    wait_vmcnt0();
-    barrier_lds();
-    // A0-3 and B0-6 of k-tile 0 (A4-7 and B7 are read in its first half)
-#pragma unroll
-    for (int f = 0; f < 4; ++f) { FP8L_RD(0, 0, f, 0); FP8L_RD(0, 0, f, 1); }
-#pragma unroll
-    for (int f = 0; f < 7; ++f) { FP8L_RD(0, 1, f, 0); FP8L_RD(0, 1, f, 1); }
-#ifdef FP8L_PHASE_TIMING
-    ph_ta = __builtin_amdgcn_s_memtime();
-    ph_ra = __builtin_amdgcn_s_memrealtime();
-#endif
-    int t = 0;
-    // k-tiles with a DMA of k-tile t+2 into the stage just drained
-    for (; t + 2 < nk; ++t) {
-      const int st = t & 1;
-      const int stn = st ^ 1;
-      const int kt2 = t + 2;
-      FP8L_H1(st)
-      FP8L_SYNC()
-      FP8L_H2(stn, st, kt2)
-    }
-    // the last one or two k-tiles: no DMA (the reads for k-tile nk fetch
-    // stale stage data into fragments that no MFMA uses)
-    for (; t < nk; ++t) {
-      const int st = t & 1;
-      const int stn = st ^ 1;
-      FP8L_H1(st)
-      FP8L_SYNC()
-      FP8L_H2N(stn)
-    }
-  }
-#undef FP8L_SYNC
-#undef FP8L_H2N
-#undef FP8L_H2
-#undef FP8L_H1
-#undef FP8L_E
-#undef FP8L_M
-#undef FP8L_MF
-#undef FP8L_RD
-#undef FP8L_DMA1
-
-#ifdef FP8L_PHASE_TIMING
-  const unsigned long long ph_t1 = __builtin_amdgcn_s_memtime();
-  const unsigned long long ph_r1 = __builtin_amdgcn_s_memrealtime();
-#endif
-  // ---- epilogue, staged through LDS: after one barrier every wave is done
-  // with the operand stages; each wave writes its scaled bf16 128 x 128 tile
-  // to its own region (rows padded to 272 bytes), then stores whole rows
-  // with 16-byte chunks (16 lanes per 256-byte row).
-  wait_lgkm0();
-  barrier_lds();
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  uint8_t *ep = lds + wave * EP_WAVE;
-  const float *inv = reinterpret_cast<const float *>(lds + INV_OFF);
-  const float inv_a0 = RW ? 0.f : 1.0f / sa[0];
-  const float inv_b0 = RW ? 0.f : 1.0f / sb[0];
-  // lane-derived values, recomputed here from an opaque copy of the thread
-  // index rather than kept live in registers across the main loop
-  int tid_e = tid;
-  asm volatile("" : "+v"(tid_e));
-  const int lane_e = tid_e & 63;
-  const int nq = (lane_e >> 4) * 4;     // first of the lane's 4 n in a block
-  if (F32) {
-    // fp32 output: two passes of 64 rows x 128 columns per wave (rows of
-    // 512 B padded to 528 B; 4 x 33 KB fits below the rowwise scale table);
-    // stores: 2 rows x 512 B per instruction, 32 lanes per row
-    constexpr int EPF_STRIDE = 528;
-    constexpr int EPF_WAVE = 64 * EPF_STRIDE;
-    static_assert(4 * EPF_WAVE <= INV_OFF, "fp32 staging overlaps the scale table");
-    uint8_t *epf = lds + wave * EPF_WAVE;
-    const int fcol = n0 + wn * WN + (lane_e & 31) * 4;
-    const bool fcol_ok = fcol < N;      // N % 16 == 0: all 4 columns or none
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int ii = 0; ii < NF / 2; ++ii) {
-        const int i = h * (NF / 2) + ii;
-        const int ml = ii * FR + (lane_e & 15);         // row within the pass
-        const float inv_a = RW ? inv[wm * WM + i * FR + (lane_e & 15)] : inv_a0;
-#pragma unroll
-        for (int j = 0; j < NF; ++j) {
-          const int nl = j * FR + nq;
-          v4f ib = {inv_b0, inv_b0, inv_b0, inv_b0};
-          if (RW) ib = *reinterpret_cast<const v4f *>(inv + BM + wn * WN + nl);
-          const v4f v = {(acc[j][i][0] * inv_a) * ib[0], (acc[j][i][1] * inv_a) * ib[1],
-                         (acc[j][i][2] * inv_a) * ib[2], (acc[j][i][3] * inv_a) * ib[3]};
-          *reinterpret_cast<v4f *>(epf + ml * EPF_STRIDE + nl * 4) = v;
-        }
-      }
-      const int frow0 = m0 + wm * WM + h * 64 + (lane_e >> 5);
-#pragma unroll
-      for (int it0 = 0; it0 < 32; it0 += 8) {
-        v4u v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int r = (it0 + u) * 2 + (lane_e >> 5);
-          v[u] = *reinterpret_cast<const v4u *>(epf + r * EPF_STRIDE + (lane_e & 31) * 16);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int row = frow0 + (it0 + u) * 2;
-          const uint32_t off = (fcol_ok && row < M) ? (uint32_t)((row * N + fcol) * 4) : OOB_C;
-          __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off, 0, C_STORE_AUX);
-        }
-      }
-    }
-    return;
-  }
-  // rowwise: the lane's reciprocal scales, read from LDS once here (the
-  // staging stores below write LDS too, so reads inside that loop would be
-  // repeated for every block)
-  float inv_ar[NF];
-  v4f inv_br[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    inv_ar[f] = RW ? inv[wm * WM + f * FR + (lane_e & 15)] : inv_a0;
-    inv_br[f] = (v4f){inv_b0, inv_b0, inv_b0, inv_b0};
-    if (RW) inv_br[f] = *reinterpret_cast<const v4f *>(inv + BM + wn * WN + f * FR + nq);
-  }
-#pragma unroll
-  for (int i = 0; i < NF; ++i) {
-    const int ml = i * FR + (lane_e & 15);              // row within the wave tile
-    const float inv_a = inv_ar[i];
-#pragma unroll
-    for (int j = 0; j < NF; ++j) {
-      const int nl = j * FR + nq;                       // col within the wave tile
-      const v4f ib = inv_br[j];
-      f32x2 v01 = {(acc[j][i][0] * inv_a) * ib[0], (acc[j][i][1] * inv_a) * ib[1]};
-      f32x2 v23 = {(acc[j][i][2] * inv_a) * ib[2], (acc[j][i][3] * inv_a) * ib[3]};
-      const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
-      const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
-      *reinterpret_cast<uint2 *>(ep + ml * EP_STRIDE + nl * 2) = make_uint2(p01, p23);
-    }
-  }
-  // store pass: 4 batches of 8 instructions; instruction u of batch it0
-  // covers tile rows (it0 + u) * 4 + lane / 16, 8 columns from (lane % 16) * 8
-  const int srow = m0 + wm * WM + (lane_e >> 4);
-  const int scol = n0 + wn * WN + (lane_e & 15) * 8;
-  const bool col_ok = scol < N;        // N % 16 == 0: all 8 columns or none
-  const int rows_left = M - srow;
-  const uint32_t soff0 = (uint32_t)((srow * N + scol) * 2);
-  const uint32_t row_step = (uint32_t)(8 * N);   // 4 rows of bf16
-#pragma unroll
-  for (int it0 = 0; it0 < WM * WN * 2 / 16 / 64; it0 += 8) {
-    v4u v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int id = (it0 + u) * 64 + lane_e;
-      v[u] = *reinterpret_cast<const v4u *>(ep + (id >> 4) * EP_STRIDE + (id & 15) * 16);
-    }
-    uint32_t off[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool ok = col_ok && (it0 + u) * 4 < rows_left;
-      off[u] = ok ? soff0 + (uint32_t)(it0 + u) * row_step : OOB_C;
-    }
-    if (ACC) {
-      // the bf16 values already in C (offsets outside read as 0), added in
-      // fp32 and rounded once to bf16 (round to nearest even)
-      v4u cin[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) cin[u] = __builtin_amdgcn_raw_buffer_load_b128(rsC, off[u], 0, 0);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t x = v[u][d], y = cin[u][d];
-          const f32x2 sum = {__uint_as_float(x << 16) + __uint_as_float(y << 16),
-                             __uint_as_float(x & 0xFFFF0000u) + __uint_as_float(y & 0xFFFF0000u)};
-          v[u][d] = __builtin_bit_cast(uint32_t, __builtin_convertvector(sum, bf16x2));
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off[u], 0, C_STORE_AUX);
-  }
-#ifdef FP8L_PHASE_TIMING
-  if (tid == 0 && blockIdx.x < PHASE_MAX_BLOCKS) {
-    const unsigned long long ph_t2 = __builtin_amdgcn_s_memtime();
-    const unsigned long long ph_r2 = __builtin_amdgcn_s_memrealtime();
-    unsigned long long *d = g_phase + (size_t)blockIdx.x * 8;
-    d[0] = ph_t0; d[1] = ph_r0; d[2] = ph_ta; d[3] = ph_ra;
-    d[4] = ph_t1; d[5] = ph_r1; d[6] = ph_t2; d[7] = ph_r2;
-  }
-#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -688,7 +240,7 @@ __device__ __forceinline__ int hw_lane() {
 // to the XCDs round-robin (b on XCD x = b % 8, the l-th of its nx, l =
 // b / 8), and each XCD works through its own contiguous share of every
 // problem's grouped tile order, problem after problem, as the XCD's blocks
-// would with one workgroup per tile (tile_of_block).  Without a schedule the
+// would with one workgroup per tile dealt round-robin.  Without a schedule the
 // XCD's workgroups take positions l, l + nx, l + 2 nx, ... of that sequence;
 // with one (g.balanced) workgroup l runs the count of tiles of problem p
 // that its entry gives, at the positions sched::position assigns.  Either
@@ -737,6 +289,14 @@ __device__ __forceinline__ TileCoord decode_tile(const GemmGroup &g, int b, int 
   return {0, 0, 0, false};
 }
 
+// KFULL: K % 128 == 0 (no K tail, no per-chunk K check).  RW: rowwise
+// scales (sa[M], sb[N]) instead of one scale per operand.  F32: fp32 output
+// (the scaled value before bf16 rounding) instead of bf16.  FA: code format
+// of A (0 = E4M3, 1 = E5M2 gradients); B is E4M3.  The instruction's
+// format selectors apply to its first and second source operand, here the
+// B and the A fragment.  ACC (bf16 output only): C holds a bf16 matrix on
+// entry and receives bf16(fl32(C) + fl32(bf16 result)), the sum of two
+// gradient contributions as bf16 tensors add.
 template <bool KFULL, bool RW, bool F32, int FA, bool ACC>
 __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
   static_assert(!(F32 && ACC), "accumulation is into a bf16 output");
@@ -752,7 +312,9 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 
   // ---- DMA cursor: the unit (tile, k-tile) whose operands load next.  Wave
   // w, instruction q (0..7 A, 8..15 B) fills slab rows w*64 + (q&7)*8 +
-  // lane/8, chunk (lane%8) ^ (lane/8) ^ (q&1), as in k_gemm_fp8_tn.  The
+  // lane/8, 16-byte chunk (lane%8) ^ (lane/8) ^ (q&1): row r keeps logical
+  // chunk c at physical chunk c ^ h(r), h(r) = (r & 7) ^ ((r >> 3) & 1), so
+  // lane i loads logical chunk (i % 8) ^ (i / 8) ^ (q & 1).  The
   // tile's first row is in the buffer resource (base A + m0 K, M - m0 rows),
   // so the per-lane offsets depend only on K, and rows past the matrix fail
   // the bounds check on the vector offset alone (they read as zero).
@@ -845,8 +407,10 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     dma16((Q) >= 8 ? d_rsB : d_rsA, dst_, kok_ ? voff[Q] : OOB, k0_);             \
   } while (0)
 
-  // ---- fragment reads (as in k_gemm_fp8_tn); the per-lane offsets are
-  // set at the top of each tile
+  // ---- fragment reads: fragment f of A is rows wm*128 + f*16 + lane%16,
+  // lane l reads logical chunks 2(l/16) and 2(l/16)+1 of its row (h(row)
+  // depends only on lane%16); the per-lane offsets are set at the top of
+  // each tile
   int fArow, fBrow, fc0, fc1;
   v8i fa[NF], fb[NF];
   v4f acc[NF][NF];   // [j: n block][i: m block]
@@ -1213,14 +777,12 @@ hipError_t launch_group(const GemmDesc *d, int count, int rowwise, hipStream_t s
   int order[MAX_GROUP], n_order = 0;
   for (int i = 0; i < count; ++i)
     if (d[i].M != 0 && d[i].N != 0) order[n_order++] = i;
-#if FP8L_GEMM_PERSISTENT
   for (int a = 1; a < n_order; ++a)
     for (int b = a; b > 0 && d[order[b]].K > d[order[b - 1]].K; --b) {
       const int t = order[b];
       order[b] = order[b - 1];
       order[b - 1] = t;
     }
-#endif
   for (int o = 0; o < n_order; ++o) {
     const int i = order[o];
     const int c = g.count++;
@@ -1234,13 +796,11 @@ hipError_t launch_group(const GemmDesc *d, int count, int rowwise, hipStream_t s
     g.K[c] = (int)d[i].K;
     g.tiles_m[c] = (int)((d[i].M + BM - 1) / BM);
     g.tiles_n[c] = (int)((d[i].N + BN - 1) / BN);
-    g.first[c] = blocks;
     blocks += g.tiles_m[c] * g.tiles_n[c];
     kfull = kfull && d[i].K % BK == 0;
   }
   if (blocks == 0) return hipSuccess;
   g.total = blocks;
-#if FP8L_GEMM_PERSISTENT
   // one workgroup per compute unit (256 on gfx950), each walking its tiles
   constexpr int kComputeUnits = 256;
   auto kern = rowwise ? (kfull ? k_gemm_fp8_pers<true, true, F32, FA, ACC>
@@ -1268,13 +828,6 @@ hipError_t launch_group(const GemmDesc *d, int count, int rowwise, hipStream_t s
         }
     }
   }
-#else
-  auto kern = rowwise ? (kfull ? k_gemm_fp8_tn<true, true, F32, FA, ACC>
-                               : k_gemm_fp8_tn<false, true, F32, FA, ACC>)
-                      : (kfull ? k_gemm_fp8_tn<true, false, F32, FA, ACC>
-                               : k_gemm_fp8_tn<false, false, F32, FA, ACC>);
-  const int grid = blocks;
-#endif
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(THREADS), 0, stream, g);
   return hipGetLastError();
 }
