@@ -226,6 +226,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// A wave-uniform float read through the scalar cache (s_load): its wait
+// counts on lgkmcnt.  A vector load's wait would count on vmcnt, which
+// completes in issue order, and so also wait for the operand transfers in
+// flight before it.
+__device__ __forceinline__ float scalar_load(const float *p) {
+  return *(const __attribute__((address_space(4))) float *)p;
+}
+
 // This lane's index in its wave (0..63), read from the hardware at the
 // point of use (v_mbcnt over a full mask).  Volatile, so the compiler
 // neither keeps an earlier copy live across the loops (nor spills one) to
@@ -633,8 +641,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     const int lane_e = hw_lane();
     const int ml16 = lane_e & 15;                 // row within a 16-row block
     const int nq = (lane_e >> 4) * 4;             // first of the lane's 4 columns in a block
-    const float inv_a0 = RW ? 0.f : 1.0f / sa[0];
-    const float inv_b0 = RW ? 0.f : 1.0f / sb[0];
+    const float inv_a0 = RW ? 0.f : 1.0f / scalar_load(sa);
+    const float inv_b0 = RW ? 0.f : 1.0f / scalar_load(sb);
     float inv_ar[NF];
     v4f inv_br[NF];
 #pragma unroll
