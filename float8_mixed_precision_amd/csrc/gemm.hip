@@ -105,7 +105,7 @@ constexpr int FR = 16;                   // rows per fragment
 constexpr int NF = WM / FR;              // fragments per operand per wave (8)
 constexpr int SLAB = BM * BK;            // 32 KB
 constexpr int STAGE_BYTES = 2 * SLAB;    // 64 KB: A slab, then B slab
-constexpr int INV_BYTES = (BM + BN) * 4;  // rowwise: 1/sa of the tile's rows, 1/sb of its cols
+constexpr int SCALE_BYTES = (BM + BN) * 4;  // rowwise: sa of the tile's rows, then sb of its cols
 constexpr int GROUP_M = 4;
 constexpr int NUM_XCD = 8;
 constexpr uint32_t OOB = 0x80000000u;    // operand offset that reads as zero
@@ -213,11 +213,14 @@ __device__ __forceinline__ T pick(const T (&v)[MAX_GROUP], int i) {
 // many are resident at once.
 constexpr int EPI_OFF = 2 * STAGE_BYTES;        // 128 KB
 constexpr int EPI_WAVE_BYTES = 8 * 1024;        // per wave: 32 rows x 256 B
-constexpr int EPI_BYTES = 4 * EPI_WAVE_BYTES;   // 32 KB (rowwise: inverse scales first)
-static_assert(INV_BYTES <= EPI_BYTES, "inverse scales fit the epilogue region");
+constexpr int EPI_BYTES = 4 * EPI_WAVE_BYTES;   // 32 KB (rowwise: each wave's scales first)
+static_assert(SCALE_BYTES <= EPI_WAVE_BYTES, "a tile's scales fit one wave's staging");
 // epilogue stores left in flight when the next tile's first k-tile waits for
 // its operands (bf16: 4 passes x 8 stores per lane)
 constexpr int EPI_STORES = 32;
+// rowwise: transfers of a tile's scales, issued at its top after the
+// previous epilogue's stores
+constexpr int SCALE_DMAS = 2;
 
 // s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding)
 template <int N>
@@ -528,7 +531,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   uint8_t *epi = lds + EPI_OFF + wave * EPI_WAVE_BYTES;
-  const float *inv = reinterpret_cast<const float *>(lds + EPI_OFF);
   int st = 0;          // stage of the current unit
 #pragma unroll
   for (int j = 0; j < NF; ++j)
@@ -557,14 +559,22 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     const unsigned long long ph_r0 = __builtin_amdgcn_s_memrealtime();
     unsigned long long ph_ta = ph_t0, ph_ra = ph_r0;
 #endif
-    // rowwise: the tile's 512 reciprocal scales into the epilogue region
-    // (free since the previous tile's closing barrier; read after the next
-    // barrier)
+    // rowwise: the tile's 256 row and 256 column scales, as stored, go by
+    // DMA into the first 2 KB of this wave's epilogue staging, which no
+    // other wave touches and whose previous contents this wave has read.
+    // They arrive with the operands (the waits below count them) and become
+    // reciprocals at the epilogue; nothing waits for them here.  Rows and
+    // columns past the matrix read as zero (dimensions are multiples of 16,
+    // so a lane's 4 scales are all inside or all outside).
     if (RW) {
-      const int t = wave * 64 + hw_lane();
-      float *w = reinterpret_cast<float *>(lds + EPI_OFF);
-      w[t] = m0 + t < M ? 1.0f / sa[m0 + t] : 0.f;
-      w[BM + t] = n0 + t < N ? 1.0f / sb[n0 + t] : 0.f;
+      const uint32_t tab = lds_base + (uint32_t)(EPI_OFF + wave * EPI_WAVE_BYTES);
+      const uint32_t lo = (uint32_t)hw_lane() * 16;
+      dma16(__builtin_amdgcn_make_buffer_rsrc((void *)(sa + m0), (short)0, (M - m0) * 4,
+                                              0x00020000),
+            tab, lo, 0);
+      dma16(__builtin_amdgcn_make_buffer_rsrc((void *)(sb + n0), (short)0, (N - n0) * 4,
+                                              0x00020000),
+            tab + BM * 4, lo, 0);
     }
     // the cursor's per-lane offsets and the fragment offsets, recomputed
     // here from the lane index instead of being kept (or spilled) across the
@@ -595,12 +605,14 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       // reaches the loop, so every accumulator block stays in its AGPRs)
       // every k-tile but the last reads the next one's first fragments and
       // loads the one after.  The first waits for its successor's operands,
-      // issued before the previous tile's epilogue, whose stores may still be
-      // in flight behind them (vmcnt counts in issue order): all but those.
+      // issued before the previous tile's epilogue, whose stores (and, for
+      // rowwise scales, this tile's scale transfers) may still be in flight
+      // behind them (vmcnt counts in issue order): all but those.  The
+      // second waits for everything, the scale transfers included.
       for (int t = 0; t < nk - 1; ++t) {
         FP8P_H1(st)
         if (t == 0 && !F32)
-          wait_vmcnt<EPI_STORES>();
+          wait_vmcnt<EPI_STORES + (RW ? SCALE_DMAS : 0)>();
         else
           wait_vmcnt0();
         wait_lgkm0();
@@ -616,7 +628,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 #endif
       }
       FP8P_H1(st)
-      if (nk == 1 && !F32)
+      if (nk == 1 && !F32 && !RW)
         wait_vmcnt<EPI_STORES>();
       else
         wait_vmcnt0();
@@ -626,7 +638,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       FP8P_DADV();
       st ^= 1;
     } else {
-      if (RW) barrier_lds();                      // the inverse scales are written
+      if (RW) wait_vmcnt0();                      // the scales have arrived
     }
 #ifdef FP8L_PHASE_TIMING
     const unsigned long long ph_t1 = __builtin_amdgcn_s_memtime();
@@ -643,15 +655,26 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     const int nq = (lane_e >> 4) * 4;             // first of the lane's 4 columns in a block
     const float inv_a0 = RW ? 0.f : 1.0f / scalar_load(sa);
     const float inv_b0 = RW ? 0.f : 1.0f / scalar_load(sb);
+    float *tab = reinterpret_cast<float *>(epi);  // rowwise: the tile's scales
+    if (RW) {
+      // the wave's 128 row scales (lanes 0-31) and 128 column scales (lanes
+      // 32-63), 4 per lane, to reciprocals in place; one wave's LDS
+      // accesses run in order, so its reads below see them
+      const int e = lane_e < 32 ? wm * WM + lane_e * 4 : BM + wn * WN + (lane_e - 32) * 4;
+      const v4f s = *reinterpret_cast<const v4f *>(tab + e);
+      *reinterpret_cast<v4f *>(tab + e) = (v4f){1.0f / s.x, 1.0f / s.y, 1.0f / s.z, 1.0f / s.w};
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     float inv_ar[NF];
     v4f inv_br[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      inv_ar[f] = RW ? inv[wm * WM + f * FR + ml16] : inv_a0;
+      inv_ar[f] = RW ? tab[wm * WM + f * FR + ml16] : inv_a0;
       inv_br[f] = (v4f){inv_b0, inv_b0, inv_b0, inv_b0};
-      if (RW) inv_br[f] = *reinterpret_cast<const v4f *>(inv + BM + wn * WN + f * FR + nq);
+      if (RW) inv_br[f] = *reinterpret_cast<const v4f *>(tab + BM + wn * WN + f * FR + nq);
     }
-    if (RW) barrier_lds();                        // every wave holds its scales
     if (F32) {
       // one 16-row block per pass: 16 rows x 512 B (32 chunks per row)
 #pragma unroll
@@ -747,14 +770,9 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       d[4] = ph_t1; d[5] = ph_r1; d[6] = ph_t2; d[7] = ph_r2;
     }
 #endif
-    // rowwise: every wave is done with the epilogue region before the next
-    // tile's inverse scales overwrite it.  Otherwise a wave stages only in
-    // its own part of that region, and the next tile's operands were made
-    // visible by the barrier of this tile's last k-tile: no barrier here.
-    if (RW) {
-      wait_lgkm0();
-      barrier_lds();
-    }
+    // a wave stages (and keeps its rowwise scales) only in its own part of
+    // the epilogue region, and the next tile's operands were made visible by
+    // the barrier of this tile's last k-tile: no barrier here
   }
 #undef FP8P_H2D
 #undef FP8P_H2
