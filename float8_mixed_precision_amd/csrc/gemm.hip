@@ -146,7 +146,10 @@ __device__ __forceinline__ void barrier_lds() {
 // kernel uses it); clang warns that it does not track reserved registers.
 // The LDS address is wave-uniform; readfirstlane keeps it in a scalar
 // register where the compiler has placed it in a vector one (it folds away
-// where the value is already scalar).
+// where the value is already scalar).  The compiler keeps the 32 addresses
+// of a k-tile's transfers (16 per stage) in scalar registers across the
+// loop; adding a constant inside the asm instead saved those registers but
+// cost the loop an instruction per transfer (~20 cycles per k-tile).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr,
@@ -214,13 +217,18 @@ __device__ __forceinline__ T pick(const T (&v)[MAX_GROUP], int i) {
 constexpr int EPI_OFF = 2 * STAGE_BYTES;        // 128 KB
 constexpr int EPI_WAVE_BYTES = 8 * 1024;        // per wave: 32 rows x 256 B
 constexpr int EPI_BYTES = 4 * EPI_WAVE_BYTES;   // 32 KB (rowwise: each wave's scales first)
-static_assert(SCALE_BYTES <= EPI_WAVE_BYTES, "a tile's scales fit one wave's staging");
 // epilogue stores left in flight when the next tile's first k-tile waits for
 // its operands (bf16: 4 passes x 8 stores per lane)
 constexpr int EPI_STORES = 32;
-// rowwise: transfers of a tile's scales, issued at its top after the
-// previous epilogue's stores
+// Rowwise scales.  Each wave keeps two scale tables at the start of its
+// staging (tiles of even and odd index) and stages its rowwise epilogues in
+// the second half.  A tile's scales are transferred two tiles ahead, after
+// the stores of an epilogue (SCALE_DMAS transfers, always issued), and
+// become reciprocals at the end of the epilogue before it.
 constexpr int SCALE_DMAS = 2;
+constexpr int RW_STAGE_OFF = EPI_WAVE_BYTES / 2;
+static_assert(2 * SCALE_BYTES <= RW_STAGE_OFF, "two scale tables below the rowwise staging");
+static_assert(EPI_WAVE_BYTES == 64 * BK, "a wave's staging is at its operand offset + EPI_OFF");
 
 // s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding)
 template <int N>
@@ -245,6 +253,18 @@ __device__ __forceinline__ int hw_lane() {
   int v;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
   return v;
+}
+
+// Four reciprocals (IEEE division, as 1/s is computed everywhere else).
+__device__ __forceinline__ v4f recip4(v4f s) {
+  return (v4f){1.0f / s.x, 1.0f / s.y, 1.0f / s.z, 1.0f / s.w};
+}
+
+// The 16-byte slot of a scale table (row scales, then column scales) whose
+// 4 scales lane l of wave (wm, wn) turns into reciprocals: lanes 0-31 the
+// wave's 128 rows, lanes 32-63 its 128 columns.
+__device__ __forceinline__ int rcp_slot(int l, int wm, int wn) {
+  return l + (l < 32 ? wm * (WM / 4) : (BM + wn * WN) / 4 - 32);
 }
 
 // Tile i (i = 0, 1, ...) of persistent workgroup b.  Workgroups are dealt
@@ -417,6 +437,25 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
                           ((Q) >= 8 ? SLAB : 0) + ((Q) & 7) * 1024);              \
     dma16((Q) >= 8 ? d_rsB : d_rsA, dst_, kok_ ? voff[Q] : OOB, k0_);             \
   } while (0)
+  // FP8P_SCALES: rowwise: the 256 row and 256 column scales of the tile at
+  // (PI, M0, N0), as stored, by DMA into this wave's scale table BUF (a wave
+  // writes and reads only its own).  Rows and columns past the matrix read
+  // as zero (dimensions are multiples of 16, so a lane's 4 scales are all
+  // inside or all outside); OK false reads nothing and writes zeros, so the
+  // count of transfers stays fixed.
+#define FP8P_SCALES(OK, PI, M0, N0, BUF)                                          \
+  do {                                                                            \
+    const uint32_t base_ = wave_dst + (uint32_t)(EPI_OFF + (BUF) * SCALE_BYTES);  \
+    const uint32_t lo_ = (uint32_t)hw_lane() * 16;                                \
+    dma16(__builtin_amdgcn_make_buffer_rsrc(                                      \
+              (void *)(pick(g.sa, PI) + (M0)), (short)0,                          \
+              (OK) ? (pick(g.M, PI) - (M0)) * 4 : 0, 0x00020000),                 \
+          base_, lo_, 0);                                                         \
+    dma16(__builtin_amdgcn_make_buffer_rsrc(                                      \
+              (void *)(pick(g.sb, PI) + (N0)), (short)0,                          \
+              (OK) ? (pick(g.N, PI) - (N0)) * 4 : 0, 0x00020000),                 \
+          base_ + BM * 4, lo_, 0);                                                \
+  } while (0)
 
   // ---- fragment reads: fragment f of A is rows wm*128 + f*16 + lane%16,
   // lane l reads logical chunks 2(l/16) and 2(l/16)+1 of its row (h(row)
@@ -525,12 +564,27 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     for (int q = 0; q < 16; ++q) FP8P_DMA1(1, q);
     FP8P_DADV();
   }
+  // rowwise: the first two tiles' scales
+  if (RW) {
+    FP8P_SCALES(a_ok, a_pi, a_m0, a_n0, 0);
+    FP8P_SCALES(b_ok, b_pi, b_m0, b_n0, 1);
+  }
   wait_vmcnt0();
   barrier_lds();
 
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   uint8_t *epi = lds + EPI_OFF + wave * EPI_WAVE_BYTES;
+  // rowwise: the entry of table BUF that this lane turns into reciprocals:
+  // 4 of the wave's 128 row scales (lanes 0-31) or 128 column scales (lanes
+  // 32-63).  One wave's LDS accesses run in order, so its later reads see
+  // what it wrote.
+#define FP8P_RCP_AT(BUF)                                                          \
+  (reinterpret_cast<v4f *>(epi + (BUF) * SCALE_BYTES) + rcp_slot(hw_lane(), wm, wn))
+  if (RW) {                                       // tile 0's scales
+    v4f *r_ = FP8P_RCP_AT(0);
+    *r_ = recip4(*r_);
+  }
   int st = 0;          // stage of the current unit
 #pragma unroll
   for (int j = 0; j < NF; ++j)
@@ -559,23 +613,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     const unsigned long long ph_r0 = __builtin_amdgcn_s_memrealtime();
     unsigned long long ph_ta = ph_t0, ph_ra = ph_r0;
 #endif
-    // rowwise: the tile's 256 row and 256 column scales, as stored, go by
-    // DMA into the first 2 KB of this wave's epilogue staging, which no
-    // other wave touches and whose previous contents this wave has read.
-    // They arrive with the operands (the waits below count them) and become
-    // reciprocals at the epilogue; nothing waits for them here.  Rows and
-    // columns past the matrix read as zero (dimensions are multiples of 16,
-    // so a lane's 4 scales are all inside or all outside).
-    if (RW) {
-      const uint32_t tab = lds_base + (uint32_t)(EPI_OFF + wave * EPI_WAVE_BYTES);
-      const uint32_t lo = (uint32_t)hw_lane() * 16;
-      dma16(__builtin_amdgcn_make_buffer_rsrc((void *)(sa + m0), (short)0, (M - m0) * 4,
-                                              0x00020000),
-            tab, lo, 0);
-      dma16(__builtin_amdgcn_make_buffer_rsrc((void *)(sb + n0), (short)0, (N - n0) * 4,
-                                              0x00020000),
-            tab + BM * 4, lo, 0);
-    }
     // the cursor's per-lane offsets and the fragment offsets, recomputed
     // here from the lane index instead of being kept (or spilled) across the
     // epilogue
@@ -606,8 +643,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       // every k-tile but the last reads the next one's first fragments and
       // loads the one after.  The first waits for its successor's operands,
       // issued before the previous tile's epilogue, whose stores (and, for
-      // rowwise scales, this tile's scale transfers) may still be in flight
-      // behind them (vmcnt counts in issue order): all but those.  The
+      // rowwise scales, the scale transfers after them) may still be in
+      // flight behind them (vmcnt counts in issue order): all but those.  The
       // second waits for everything, the scale transfers included.
       for (int t = 0; t < nk - 1; ++t) {
         FP8P_H1(st)
@@ -628,6 +665,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 #endif
       }
       FP8P_H1(st)
+      // (rowwise: the next tile's scales, issued after the previous
+      // epilogue's stores, must have arrived by the end of this epilogue)
       if (nk == 1 && !F32 && !RW)
         wait_vmcnt<EPI_STORES>();
       else
@@ -637,8 +676,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       FP8P_H2D(st)
       FP8P_DADV();
       st ^= 1;
-    } else {
-      if (RW) wait_vmcnt0();                      // the scales have arrived
     }
 #ifdef FP8L_PHASE_TIMING
     const unsigned long long ph_t1 = __builtin_amdgcn_s_memtime();
@@ -655,27 +692,52 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     const int nq = (lane_e >> 4) * 4;             // first of the lane's 4 columns in a block
     const float inv_a0 = RW ? 0.f : 1.0f / scalar_load(sa);
     const float inv_b0 = RW ? 0.f : 1.0f / scalar_load(sb);
-    float *tab = reinterpret_cast<float *>(epi);  // rowwise: the tile's scales
-    if (RW) {
-      // the wave's 128 row scales (lanes 0-31) and 128 column scales (lanes
-      // 32-63), 4 per lane, to reciprocals in place; one wave's LDS
-      // accesses run in order, so its reads below see them
-      const int e = lane_e < 32 ? wm * WM + lane_e * 4 : BM + wn * WN + (lane_e - 32) * 4;
-      const v4f s = *reinterpret_cast<const v4f *>(tab + e);
-      *reinterpret_cast<v4f *>(tab + e) = (v4f){1.0f / s.x, 1.0f / s.y, 1.0f / s.z, 1.0f / s.w};
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+    // tensorwise: one reciprocal per operand
     float inv_ar[NF];
     v4f inv_br[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      inv_ar[f] = RW ? tab[wm * WM + f * FR + ml16] : inv_a0;
+      inv_ar[f] = inv_a0;
       inv_br[f] = (v4f){inv_b0, inv_b0, inv_b0, inv_b0};
-      if (RW) inv_br[f] = *reinterpret_cast<const v4f *>(tab + BM + wn * WN + f * FR + nq);
     }
-    if (F32) {
+    // rowwise: the tile's reciprocal scales
+    const float *tab = reinterpret_cast<const float *>(epi + (tile & 1) * SCALE_BYTES);
+    uint8_t *stg = epi + RW_STAGE_OFF;            // rowwise staging
+    if (RW && F32) {
+      // rowwise fp32: the tile's columns in two halves of 64, one 16-row
+      // block per pass: 16 rows x 256 B (row r's 16-byte chunk c at
+      // c ^ (r % 16)); the reciprocals are read from the table where they
+      // are used
+#pragma unroll
+      for (int jh = 0; jh < 2; ++jh) {
+        const int col = n0 + wn * WN + jh * 64 + (lane_e & 15) * 4;
+        const bool col_ok = col < N;
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+          const float ia = tab[wm * WM + i * FR + ml16];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int j = jh * 4 + jj;
+            const v4f ib = *reinterpret_cast<const v4f *>(tab + BM + wn * WN + j * FR + nq);
+            const v4f v = {(acc[j][i][0] * ia) * ib[0], (acc[j][i][1] * ia) * ib[1],
+                           (acc[j][i][2] * ia) * ib[2], (acc[j][i][3] * ia) * ib[3]};
+            acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};  // cleared for the next tile
+            const int ch = (jj * 4 + (lane_e >> 4)) ^ ml16;
+            *reinterpret_cast<v4f *>(stg + ml16 * 256 + ch * 16) = v;
+          }
+          const int row0 = m0 + wm * WM + i * FR;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int r = u * 4 + (lane_e >> 4);
+            const v4u v = *reinterpret_cast<const v4u *>(
+                stg + r * 256 + (((lane_e & 15) ^ r) * 16));
+            const uint32_t off = (col_ok && row0 + r < M) ? (uint32_t)(((row0 + r) * N + col) * 4)
+                                                          : OOB_C;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, C_STORE_AUX);
+          }
+        }
+      }
+    } else if (F32) {
       // one 16-row block per pass: 16 rows x 512 B (32 chunks per row)
 #pragma unroll
       for (int i = 0; i < NF; ++i) {
@@ -699,6 +761,74 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
           const uint32_t off = (col_ok && row0 + r < M) ? (uint32_t)(((row0 + r) * N + col) * 4)
                                                         : OOB_C;
           __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, C_STORE_AUX);
+        }
+      }
+    } else if (RW) {
+      // rowwise bf16: the tile's columns in two halves of 64, 32 rows x
+      // 128 B per pass (row r's 16-byte chunk c at c ^ (r % 8), its 8-byte
+      // halves swapped where r % 16 >= 8); the reciprocals are read from the
+      // table where they are used (2 row and 4 column values at a time), so
+      // that they add few registers to the epilogue's
+#pragma unroll
+      for (int jh = 0; jh < 2; ++jh) {
+        const int scol = n0 + wn * WN + jh * 64 + (lane_e & 7) * 8;
+        const bool col_ok = scol < N;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float ia0 = tab[wm * WM + 2 * p * FR + ml16];
+          const float ia1 = tab[wm * WM + (2 * p + 1) * FR + ml16];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int j = jh * 4 + jj;
+            const v4f ib = *reinterpret_cast<const v4f *>(tab + BM + wn * WN + j * FR + nq);
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+              const int i = 2 * p + ii;
+              const int ml = ii * FR + ml16;      // row within the pass
+              const float ia = ii ? ia1 : ia0;
+              f32x2 v01 = {(acc[j][i][0] * ia) * ib[0], (acc[j][i][1] * ia) * ib[1]};
+              f32x2 v23 = {(acc[j][i][2] * ia) * ib[2], (acc[j][i][3] * ia) * ib[3]};
+              acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};  // cleared for the next tile
+              const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
+              const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
+              // byte column (jj*16 + nq)*2 of the half: chunk 2jj + nq/8
+              const int ch = (2 * jj + (nq >> 3)) ^ (ml16 & 7);
+              *reinterpret_cast<uint2 *>(stg + ml * 128 + ch * 16 +
+                                         (((nq & 7) * 2) ^ ((ml16 >> 3) << 3))) =
+                  make_uint2(p01, p23);
+            }
+          }
+          // 4 instructions: rows u*8 + lane/8 of the pass, 8 columns each
+          const int srow = m0 + wm * WM + p * 32 + (lane_e >> 3);
+          v4u v[4];
+          uint32_t off[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int r = u * 8 + (lane_e >> 3);
+            v[u] = *reinterpret_cast<const v4u *>(stg + r * 128 + (((lane_e & 7) ^ (r & 7)) * 16));
+            // rows with r % 16 >= 8 (u odd) hold their halves swapped
+            if (u & 1) v[u] = (v4u){v[u].z, v[u].w, v[u].x, v[u].y};
+            const bool ok = col_ok && srow + u * 8 < M;
+            off[u] = ok ? (uint32_t)(((srow + u * 8) * N + scol) * 2) : OOB_C;
+          }
+          if (ACC) {
+            v4u cin[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) cin[u] = __builtin_amdgcn_raw_buffer_load_b128(rsC, off[u], 0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+              for (int d = 0; d < 4; ++d) {
+                const uint32_t x = v[u][d], y = cin[u][d];
+                const f32x2 sum = {__uint_as_float(x << 16) + __uint_as_float(y << 16),
+                                   __uint_as_float(x & 0xFFFF0000u) + __uint_as_float(y & 0xFFFF0000u)};
+                v[u][d] = __builtin_bit_cast(uint32_t, __builtin_convertvector(sum, bf16x2));
+              }
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off[u], 0, C_STORE_AUX);
         }
       }
     } else {
@@ -770,9 +900,21 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       d[4] = ph_t1; d[5] = ph_r1; d[6] = ph_t2; d[7] = ph_r2;
     }
 #endif
-    // a wave stages (and keeps its rowwise scales) only in its own part of
-    // the epilogue region, and the next tile's operands were made visible by
-    // the barrier of this tile's last k-tile: no barrier here
+    // rowwise: the next tile's scales (arrived: this tile's waits counted
+    // them, or with K = 0 the one here) become reciprocals, and the scales
+    // of the tile after next go into the table this tile is done with,
+    // after the stores (the next tile's first wait lets both run on).  In
+    // the k-loop (hidden between matrix instructions) the conversion made
+    // the compiler clear the accumulators twice per tile.  A wave stages and
+    // keeps its scales only in its own part of the epilogue region, and the
+    // next tile's operands were made visible by the barrier of this tile's
+    // last k-tile: no barrier here.
+    if (RW) {
+      if (nk == 0) wait_vmcnt0();
+      v4f *rn = FP8P_RCP_AT((tile + 1) & 1);
+      *rn = recip4(*rn);
+      FP8P_SCALES(b_ok, b_pi, b_m0, b_n0, tile & 1);
+    }
   }
 #undef FP8P_H2D
 #undef FP8P_H2
@@ -781,6 +923,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 #undef FP8P_M
 #undef FP8P_MF
 #undef FP8P_RD
+#undef FP8P_SCALES
+#undef FP8P_RCP_AT
 #undef FP8P_DMA1
 #undef FP8P_DADV
 #undef FP8P_DSETUP
