@@ -391,12 +391,11 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       voff[q] = (uint32_t)(row * d_K + ((q & 1) ? ce_v ^ 1 : ce_v) * 16);       \
     }                                                                           \
   } while (0)
-  // FP8P_DSETUP: the cursor enters tile d_tile.  The host orders a launch's
-  // problems by decreasing K, so a tile with K = 0 is followed by no tile
-  // that needs operands: the cursor stops there.  Past the last tile
-  // decode_tile gives problem 0's origin, which serves the empty buffers
-  // an exhausted cursor still issues its (zero-filling) transfers from, into
-  // the stage no one reads any more.
+  // FP8P_DSETUP: the cursor enters tile d_tile.  The host launches no
+  // problem with K = 0 (k_gemm_k0 writes those), so every tile has at least
+  // one k-tile.  Past the last tile decode_tile gives problem 0's origin,
+  // which serves the empty buffers an exhausted cursor still issues its
+  // (zero-filling) transfers from, into the stage no one reads any more.
 #define FP8P_DSETUP()                                                           \
   do {                                                                          \
     const bool sa_ = d_tile == cur, sb_ = d_tile == cur + 1;                    \
@@ -479,80 +478,86 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 #define FP8P_MF(J, I)                                                             \
   acc[J][I] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                   \
       fb[J], fa[I], acc[J][I], 0, FA, 0, 0, 0, 0)
-#define FP8P_M(S, I0) FP8P_MF((S) / 4, (I0) + ((((S) / 4) & 1) ? (S) % 4 : 3 - (S) % 4));
+// the same with a zero accumulator input (a tile's first k-tile)
+#define FP8P_MFZ(J, I)                                                            \
+  acc[J][I] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                   \
+      fb[J], fa[I], (v4f){0.f, 0.f, 0.f, 0.f}, 0, FA, 0, 0, 0, 0)
+// step S of a half k-tile with MF (FP8P_MF or FP8P_MFZ)
+#define FP8P_MX(MF, S, I0) MF((S) / 4, (I0) + ((((S) / 4) & 1) ? (S) % 4 : 3 - (S) % 4));
+#define FP8P_M(S, I0) FP8P_MX(FP8P_MF, S, I0)
 #define FP8P_E() __builtin_amdgcn_sched_barrier(0);
-#define FP8P_H1(ST) \
-  FP8P_M(0, 0) FP8P_RD(ST, 0, 7, 0); FP8P_E() \
-  FP8P_M(1, 0) FP8P_RD(ST, 0, 7, 1); FP8P_E() \
-  FP8P_M(2, 0) FP8P_RD(ST, 0, 6, 0); FP8P_E() \
-  FP8P_M(3, 0) FP8P_RD(ST, 0, 6, 1); FP8P_E() \
-  FP8P_M(4, 0) FP8P_RD(ST, 0, 5, 0); FP8P_E() \
-  FP8P_M(5, 0) FP8P_RD(ST, 0, 5, 1); FP8P_E() \
-  FP8P_M(6, 0) FP8P_RD(ST, 0, 4, 0); FP8P_E() \
-  FP8P_M(7, 0) FP8P_RD(ST, 0, 4, 1); FP8P_E() \
-  FP8P_M(8, 0) FP8P_RD(ST, 1, 7, 0); FP8P_E() \
-  FP8P_M(9, 0) FP8P_RD(ST, 1, 7, 1); FP8P_E() \
-  FP8P_M(10, 0) FP8P_E() FP8P_M(11, 0) FP8P_E() FP8P_M(12, 0) FP8P_E() \
-  FP8P_M(13, 0) FP8P_E() FP8P_M(14, 0) FP8P_E() FP8P_M(15, 0) FP8P_E() \
-  FP8P_M(16, 0) FP8P_E() FP8P_M(17, 0) FP8P_E() FP8P_M(18, 0) FP8P_E() \
-  FP8P_M(19, 0) FP8P_E() FP8P_M(20, 0) FP8P_E() FP8P_M(21, 0) FP8P_E() \
-  FP8P_M(22, 0) FP8P_E() FP8P_M(23, 0) FP8P_E() FP8P_M(24, 0) FP8P_E() \
-  FP8P_M(25, 0) FP8P_E() FP8P_M(26, 0) FP8P_E() FP8P_M(27, 0) FP8P_E() \
-  FP8P_M(28, 0) FP8P_E() FP8P_M(29, 0) FP8P_E() FP8P_M(30, 0) FP8P_E() \
-  FP8P_M(31, 0) FP8P_E()
-#define FP8P_H2(STN, DST) \
-  FP8P_M(0, 4) FP8P_RD(STN, 0, 3, 0); FP8P_E() \
-  FP8P_M(1, 4) FP8P_DMA1(DST, 0); FP8P_E() \
-  FP8P_M(2, 4) FP8P_RD(STN, 0, 3, 1); FP8P_E() \
-  FP8P_M(3, 4) FP8P_DMA1(DST, 1); FP8P_E() \
-  FP8P_M(4, 4) FP8P_RD(STN, 0, 2, 0); FP8P_RD(STN, 1, 0, 0); FP8P_E() \
-  FP8P_M(5, 4) FP8P_RD(STN, 1, 0, 1); FP8P_DMA1(DST, 2); FP8P_E() \
-  FP8P_M(6, 4) FP8P_RD(STN, 0, 2, 1); FP8P_E() \
-  FP8P_M(7, 4) FP8P_DMA1(DST, 3); FP8P_E() \
-  FP8P_M(8, 4) FP8P_RD(STN, 0, 1, 0); FP8P_RD(STN, 1, 1, 0); FP8P_E() \
-  FP8P_M(9, 4) FP8P_RD(STN, 1, 1, 1); FP8P_DMA1(DST, 4); FP8P_E() \
-  FP8P_M(10, 4) FP8P_RD(STN, 0, 1, 1); FP8P_E() \
-  FP8P_M(11, 4) FP8P_DMA1(DST, 5); FP8P_E() \
-  FP8P_M(12, 4) FP8P_RD(STN, 0, 0, 0); FP8P_RD(STN, 1, 2, 0); FP8P_E() \
-  FP8P_M(13, 4) FP8P_RD(STN, 1, 2, 1); FP8P_DMA1(DST, 6); FP8P_E() \
-  FP8P_M(14, 4) FP8P_RD(STN, 0, 0, 1); FP8P_E() \
-  FP8P_M(15, 4) FP8P_DMA1(DST, 7); FP8P_E() \
-  FP8P_M(16, 4) FP8P_RD(STN, 1, 3, 0); FP8P_E() \
-  FP8P_M(17, 4) FP8P_RD(STN, 1, 3, 1); FP8P_DMA1(DST, 8); FP8P_E() \
-  FP8P_M(18, 4) FP8P_E() \
-  FP8P_M(19, 4) FP8P_DMA1(DST, 9); FP8P_E() \
-  FP8P_M(20, 4) FP8P_RD(STN, 1, 4, 0); FP8P_E() \
-  FP8P_M(21, 4) FP8P_RD(STN, 1, 4, 1); FP8P_DMA1(DST, 10); FP8P_E() \
-  FP8P_M(22, 4) FP8P_E() \
-  FP8P_M(23, 4) FP8P_DMA1(DST, 11); FP8P_E() \
-  FP8P_M(24, 4) FP8P_RD(STN, 1, 5, 0); FP8P_E() \
-  FP8P_M(25, 4) FP8P_RD(STN, 1, 5, 1); FP8P_DMA1(DST, 12); FP8P_E() \
-  FP8P_M(26, 4) FP8P_E() \
-  FP8P_M(27, 4) FP8P_DMA1(DST, 13); FP8P_E() \
-  FP8P_M(28, 4) FP8P_RD(STN, 1, 6, 0); FP8P_E() \
-  FP8P_M(29, 4) FP8P_RD(STN, 1, 6, 1); FP8P_DMA1(DST, 14); FP8P_E() \
-  FP8P_M(30, 4) FP8P_E() \
-  FP8P_M(31, 4) FP8P_DMA1(DST, 15); FP8P_E()
+#define FP8P_H1(ST, MF) \
+  FP8P_MX(MF, 0, 0) FP8P_RD(ST, 0, 7, 0); FP8P_E() \
+  FP8P_MX(MF, 1, 0) FP8P_RD(ST, 0, 7, 1); FP8P_E() \
+  FP8P_MX(MF, 2, 0) FP8P_RD(ST, 0, 6, 0); FP8P_E() \
+  FP8P_MX(MF, 3, 0) FP8P_RD(ST, 0, 6, 1); FP8P_E() \
+  FP8P_MX(MF, 4, 0) FP8P_RD(ST, 0, 5, 0); FP8P_E() \
+  FP8P_MX(MF, 5, 0) FP8P_RD(ST, 0, 5, 1); FP8P_E() \
+  FP8P_MX(MF, 6, 0) FP8P_RD(ST, 0, 4, 0); FP8P_E() \
+  FP8P_MX(MF, 7, 0) FP8P_RD(ST, 0, 4, 1); FP8P_E() \
+  FP8P_MX(MF, 8, 0) FP8P_RD(ST, 1, 7, 0); FP8P_E() \
+  FP8P_MX(MF, 9, 0) FP8P_RD(ST, 1, 7, 1); FP8P_E() \
+  FP8P_MX(MF, 10, 0) FP8P_E() FP8P_MX(MF, 11, 0) FP8P_E() FP8P_MX(MF, 12, 0) FP8P_E() \
+  FP8P_MX(MF, 13, 0) FP8P_E() FP8P_MX(MF, 14, 0) FP8P_E() FP8P_MX(MF, 15, 0) FP8P_E() \
+  FP8P_MX(MF, 16, 0) FP8P_E() FP8P_MX(MF, 17, 0) FP8P_E() FP8P_MX(MF, 18, 0) FP8P_E() \
+  FP8P_MX(MF, 19, 0) FP8P_E() FP8P_MX(MF, 20, 0) FP8P_E() FP8P_MX(MF, 21, 0) FP8P_E() \
+  FP8P_MX(MF, 22, 0) FP8P_E() FP8P_MX(MF, 23, 0) FP8P_E() FP8P_MX(MF, 24, 0) FP8P_E() \
+  FP8P_MX(MF, 25, 0) FP8P_E() FP8P_MX(MF, 26, 0) FP8P_E() FP8P_MX(MF, 27, 0) FP8P_E() \
+  FP8P_MX(MF, 28, 0) FP8P_E() FP8P_MX(MF, 29, 0) FP8P_E() FP8P_MX(MF, 30, 0) FP8P_E() \
+  FP8P_MX(MF, 31, 0) FP8P_E()
+#define FP8P_H2(STN, DST, MF) \
+  FP8P_MX(MF, 0, 4) FP8P_RD(STN, 0, 3, 0); FP8P_E() \
+  FP8P_MX(MF, 1, 4) FP8P_DMA1(DST, 0); FP8P_E() \
+  FP8P_MX(MF, 2, 4) FP8P_RD(STN, 0, 3, 1); FP8P_E() \
+  FP8P_MX(MF, 3, 4) FP8P_DMA1(DST, 1); FP8P_E() \
+  FP8P_MX(MF, 4, 4) FP8P_RD(STN, 0, 2, 0); FP8P_RD(STN, 1, 0, 0); FP8P_E() \
+  FP8P_MX(MF, 5, 4) FP8P_RD(STN, 1, 0, 1); FP8P_DMA1(DST, 2); FP8P_E() \
+  FP8P_MX(MF, 6, 4) FP8P_RD(STN, 0, 2, 1); FP8P_E() \
+  FP8P_MX(MF, 7, 4) FP8P_DMA1(DST, 3); FP8P_E() \
+  FP8P_MX(MF, 8, 4) FP8P_RD(STN, 0, 1, 0); FP8P_RD(STN, 1, 1, 0); FP8P_E() \
+  FP8P_MX(MF, 9, 4) FP8P_RD(STN, 1, 1, 1); FP8P_DMA1(DST, 4); FP8P_E() \
+  FP8P_MX(MF, 10, 4) FP8P_RD(STN, 0, 1, 1); FP8P_E() \
+  FP8P_MX(MF, 11, 4) FP8P_DMA1(DST, 5); FP8P_E() \
+  FP8P_MX(MF, 12, 4) FP8P_RD(STN, 0, 0, 0); FP8P_RD(STN, 1, 2, 0); FP8P_E() \
+  FP8P_MX(MF, 13, 4) FP8P_RD(STN, 1, 2, 1); FP8P_DMA1(DST, 6); FP8P_E() \
+  FP8P_MX(MF, 14, 4) FP8P_RD(STN, 0, 0, 1); FP8P_E() \
+  FP8P_MX(MF, 15, 4) FP8P_DMA1(DST, 7); FP8P_E() \
+  FP8P_MX(MF, 16, 4) FP8P_RD(STN, 1, 3, 0); FP8P_E() \
+  FP8P_MX(MF, 17, 4) FP8P_RD(STN, 1, 3, 1); FP8P_DMA1(DST, 8); FP8P_E() \
+  FP8P_MX(MF, 18, 4) FP8P_E() \
+  FP8P_MX(MF, 19, 4) FP8P_DMA1(DST, 9); FP8P_E() \
+  FP8P_MX(MF, 20, 4) FP8P_RD(STN, 1, 4, 0); FP8P_E() \
+  FP8P_MX(MF, 21, 4) FP8P_RD(STN, 1, 4, 1); FP8P_DMA1(DST, 10); FP8P_E() \
+  FP8P_MX(MF, 22, 4) FP8P_E() \
+  FP8P_MX(MF, 23, 4) FP8P_DMA1(DST, 11); FP8P_E() \
+  FP8P_MX(MF, 24, 4) FP8P_RD(STN, 1, 5, 0); FP8P_E() \
+  FP8P_MX(MF, 25, 4) FP8P_RD(STN, 1, 5, 1); FP8P_DMA1(DST, 12); FP8P_E() \
+  FP8P_MX(MF, 26, 4) FP8P_E() \
+  FP8P_MX(MF, 27, 4) FP8P_DMA1(DST, 13); FP8P_E() \
+  FP8P_MX(MF, 28, 4) FP8P_RD(STN, 1, 6, 0); FP8P_E() \
+  FP8P_MX(MF, 29, 4) FP8P_RD(STN, 1, 6, 1); FP8P_DMA1(DST, 14); FP8P_E() \
+  FP8P_MX(MF, 30, 4) FP8P_E() \
+  FP8P_MX(MF, 31, 4) FP8P_DMA1(DST, 15); FP8P_E()
 
 // last k-tile of a tile: the DMAs only (the next tile's first fragments are
 // read after the epilogue, which keeps them out of its registers)
-#define FP8P_H2D(DST) \
-  FP8P_M(0, 4) FP8P_E() FP8P_M(1, 4) FP8P_DMA1(DST, 0); FP8P_E() \
-  FP8P_M(2, 4) FP8P_E() FP8P_M(3, 4) FP8P_DMA1(DST, 1); FP8P_E() \
-  FP8P_M(4, 4) FP8P_E() FP8P_M(5, 4) FP8P_DMA1(DST, 2); FP8P_E() \
-  FP8P_M(6, 4) FP8P_E() FP8P_M(7, 4) FP8P_DMA1(DST, 3); FP8P_E() \
-  FP8P_M(8, 4) FP8P_E() FP8P_M(9, 4) FP8P_DMA1(DST, 4); FP8P_E() \
-  FP8P_M(10, 4) FP8P_E() FP8P_M(11, 4) FP8P_DMA1(DST, 5); FP8P_E() \
-  FP8P_M(12, 4) FP8P_E() FP8P_M(13, 4) FP8P_DMA1(DST, 6); FP8P_E() \
-  FP8P_M(14, 4) FP8P_E() FP8P_M(15, 4) FP8P_DMA1(DST, 7); FP8P_E() \
-  FP8P_M(16, 4) FP8P_E() FP8P_M(17, 4) FP8P_DMA1(DST, 8); FP8P_E() \
-  FP8P_M(18, 4) FP8P_E() FP8P_M(19, 4) FP8P_DMA1(DST, 9); FP8P_E() \
-  FP8P_M(20, 4) FP8P_E() FP8P_M(21, 4) FP8P_DMA1(DST, 10); FP8P_E() \
-  FP8P_M(22, 4) FP8P_E() FP8P_M(23, 4) FP8P_DMA1(DST, 11); FP8P_E() \
-  FP8P_M(24, 4) FP8P_E() FP8P_M(25, 4) FP8P_DMA1(DST, 12); FP8P_E() \
-  FP8P_M(26, 4) FP8P_E() FP8P_M(27, 4) FP8P_DMA1(DST, 13); FP8P_E() \
-  FP8P_M(28, 4) FP8P_E() FP8P_M(29, 4) FP8P_DMA1(DST, 14); FP8P_E() \
-  FP8P_M(30, 4) FP8P_E() FP8P_M(31, 4) FP8P_DMA1(DST, 15); FP8P_E()
+#define FP8P_H2D(DST, MF) \
+  FP8P_MX(MF, 0, 4) FP8P_E() FP8P_MX(MF, 1, 4) FP8P_DMA1(DST, 0); FP8P_E() \
+  FP8P_MX(MF, 2, 4) FP8P_E() FP8P_MX(MF, 3, 4) FP8P_DMA1(DST, 1); FP8P_E() \
+  FP8P_MX(MF, 4, 4) FP8P_E() FP8P_MX(MF, 5, 4) FP8P_DMA1(DST, 2); FP8P_E() \
+  FP8P_MX(MF, 6, 4) FP8P_E() FP8P_MX(MF, 7, 4) FP8P_DMA1(DST, 3); FP8P_E() \
+  FP8P_MX(MF, 8, 4) FP8P_E() FP8P_MX(MF, 9, 4) FP8P_DMA1(DST, 4); FP8P_E() \
+  FP8P_MX(MF, 10, 4) FP8P_E() FP8P_MX(MF, 11, 4) FP8P_DMA1(DST, 5); FP8P_E() \
+  FP8P_MX(MF, 12, 4) FP8P_E() FP8P_MX(MF, 13, 4) FP8P_DMA1(DST, 6); FP8P_E() \
+  FP8P_MX(MF, 14, 4) FP8P_E() FP8P_MX(MF, 15, 4) FP8P_DMA1(DST, 7); FP8P_E() \
+  FP8P_MX(MF, 16, 4) FP8P_E() FP8P_MX(MF, 17, 4) FP8P_DMA1(DST, 8); FP8P_E() \
+  FP8P_MX(MF, 18, 4) FP8P_E() FP8P_MX(MF, 19, 4) FP8P_DMA1(DST, 9); FP8P_E() \
+  FP8P_MX(MF, 20, 4) FP8P_E() FP8P_MX(MF, 21, 4) FP8P_DMA1(DST, 10); FP8P_E() \
+  FP8P_MX(MF, 22, 4) FP8P_E() FP8P_MX(MF, 23, 4) FP8P_DMA1(DST, 11); FP8P_E() \
+  FP8P_MX(MF, 24, 4) FP8P_E() FP8P_MX(MF, 25, 4) FP8P_DMA1(DST, 12); FP8P_E() \
+  FP8P_MX(MF, 26, 4) FP8P_E() FP8P_MX(MF, 27, 4) FP8P_DMA1(DST, 13); FP8P_E() \
+  FP8P_MX(MF, 28, 4) FP8P_E() FP8P_MX(MF, 29, 4) FP8P_DMA1(DST, 14); FP8P_E() \
+  FP8P_MX(MF, 30, 4) FP8P_E() FP8P_MX(MF, 31, 4) FP8P_DMA1(DST, 15); FP8P_E()
 
   // ---- the first two units' operands (the fragments are read at the top
   // of each tile)
@@ -586,10 +591,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     *r_ = recip4(*r_);
   }
   int st = 0;          // stage of the current unit
-#pragma unroll
-  for (int j = 0; j < NF; ++j)
-#pragma unroll
-    for (int i = 0; i < NF; ++i) acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};
   for (int tile = 0;; ++tile) {
     const TileCoord tc = {a_pi, a_m0, a_n0, a_ok};
     if (!tc.valid) break;
@@ -628,7 +629,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       fc0 = ((2 * g4) ^ hr) << 4;
       fc1 = ((2 * g4 + 1) ^ hr) << 4;
     }
-    if (nk > 0) {
+    {
       // A0-3 and B0-6 of the tile's first k-tile (complete in stage st: this
       // wave waited for its part and passed a barrier since)
 #pragma unroll
@@ -636,47 +637,61 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 #pragma unroll
       for (int f = 0; f < 7; ++f) { FP8P_RD(st, 1, f, 0); FP8P_RD(st, 1, f, 1); }
     }
-    if (nk > 0) {
-      // the accumulators hold zeros here: cleared before the first tile and
-      // by the previous tile's epilogue as it read them (one definition
-      // reaches the loop, so every accumulator block stays in its AGPRs)
-      // every k-tile but the last reads the next one's first fragments and
-      // loads the one after.  The first waits for its successor's operands,
-      // issued before the previous tile's epilogue, whose stores (and, for
-      // rowwise scales, the scale transfers after them) may still be in
-      // flight behind them (vmcnt counts in issue order): all but those.  The
-      // second waits for everything, the scale transfers included.
-      for (int t = 0; t < nk - 1; ++t) {
-        FP8P_H1(st)
-        if (t == 0 && !F32)
-          wait_vmcnt<EPI_STORES + (RW ? SCALE_DMAS : 0)>();
-        else
-          wait_vmcnt0();
-        wait_lgkm0();
-        barrier_lds();
-        FP8P_H2(st ^ 1, st)
-        FP8P_DADV();
-        st ^= 1;
-#ifdef FP8L_PHASE_TIMING
-        if (t == 0) {
-          ph_ta = __builtin_amdgcn_s_memtime();
-          ph_ra = __builtin_amdgcn_s_memrealtime();
-        }
-#endif
-      }
-      FP8P_H1(st)
-      // (rowwise: the next tile's scales, issued after the previous
-      // epilogue's stores, must have arrived by the end of this epilogue)
-      if (nk == 1 && !F32 && !RW)
-        wait_vmcnt<EPI_STORES>();
+    // the last k-tile (MF: FP8P_MF, or FP8P_MFZ when it is also the first).
+    // It waits for everything but, where it follows the previous epilogue
+    // directly (K <= 128, bf16 tensorwise), that epilogue's stores (rowwise:
+    // the next tile's scales, issued after them, must have arrived by the
+    // end of this epilogue).
+#define FP8P_LAST(MF)                                                             \
+  do {                                                                            \
+    FP8P_H1(st, MF)                                                               \
+    if (nk == 1 && !F32 && !RW)                                                   \
+      wait_vmcnt<EPI_STORES>();                                                   \
+    else                                                                          \
+      wait_vmcnt0();                                                              \
+    wait_lgkm0();                                                                 \
+    barrier_lds();                                                                \
+    FP8P_H2D(st, MF)                                                              \
+    FP8P_DADV();                                                                  \
+    st ^= 1;                                                                      \
+  } while (0)
+    if (nk > 1) {
+      // the first k-tile, peeled: its matrix instructions start from a zero
+      // accumulator input, so no tile clears its 256 accumulator registers
+      // first.  It waits for its successor's operands, issued before the
+      // previous tile's epilogue, whose stores (and, for rowwise scales,
+      // the scale transfers after them) may still be in flight behind them
+      // (vmcnt counts in issue order): all but those.
+      FP8P_H1(st, FP8P_MFZ)
+      if (!F32)
+        wait_vmcnt<EPI_STORES + (RW ? SCALE_DMAS : 0)>();
       else
         wait_vmcnt0();
       wait_lgkm0();
       barrier_lds();
-      FP8P_H2D(st)
+      FP8P_H2(st ^ 1, st, FP8P_MFZ)
       FP8P_DADV();
       st ^= 1;
+#ifdef FP8L_PHASE_TIMING
+      ph_ta = __builtin_amdgcn_s_memtime();
+      ph_ra = __builtin_amdgcn_s_memrealtime();
+#endif
+      // every further k-tile but the last reads the next one's first
+      // fragments and loads the one after; each waits for everything
+      for (int t = 1; t < nk - 1; ++t) {
+        FP8P_H1(st, FP8P_MF)
+        wait_vmcnt0();
+        wait_lgkm0();
+        barrier_lds();
+        FP8P_H2(st ^ 1, st, FP8P_MF)
+        FP8P_DADV();
+        st ^= 1;
+      }
+      FP8P_LAST(FP8P_MF);
+    } else {
+      FP8P_LAST(FP8P_MFZ);                        // one k-tile (K <= 128)
     }
+#undef FP8P_LAST
 #ifdef FP8L_PHASE_TIMING
     const unsigned long long ph_t1 = __builtin_amdgcn_s_memtime();
     const unsigned long long ph_r1 = __builtin_amdgcn_s_memrealtime();
@@ -721,7 +736,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
             const v4f ib = *reinterpret_cast<const v4f *>(tab + BM + wn * WN + j * FR + nq);
             const v4f v = {(acc[j][i][0] * ia) * ib[0], (acc[j][i][1] * ia) * ib[1],
                            (acc[j][i][2] * ia) * ib[2], (acc[j][i][3] * ia) * ib[3]};
-            acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};  // cleared for the next tile
             const int ch = (jj * 4 + (lane_e >> 4)) ^ ml16;
             *reinterpret_cast<v4f *>(stg + ml16 * 256 + ch * 16) = v;
           }
@@ -746,7 +760,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
           const v4f ib = inv_br[j];
           const v4f v = {(acc[j][i][0] * inv_ar[i]) * ib[0], (acc[j][i][1] * inv_ar[i]) * ib[1],
                          (acc[j][i][2] * inv_ar[i]) * ib[2], (acc[j][i][3] * inv_ar[i]) * ib[3]};
-          acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};    // cleared for the next tile
           const int ch = (j * 4 + (lane_e >> 4)) ^ ml16;
           *reinterpret_cast<v4f *>(epi + ml16 * 512 + ch * 16) = v;
         }
@@ -788,7 +801,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
               const float ia = ii ? ia1 : ia0;
               f32x2 v01 = {(acc[j][i][0] * ia) * ib[0], (acc[j][i][1] * ia) * ib[1]};
               f32x2 v23 = {(acc[j][i][2] * ia) * ib[2], (acc[j][i][3] * ia) * ib[3]};
-              acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};  // cleared for the next tile
               const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
               const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
               // byte column (jj*16 + nq)*2 of the half: chunk 2jj + nq/8
@@ -846,7 +858,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
             const float ia = inv_ar[i];
             f32x2 v01 = {(acc[j][i][0] * ia) * ib[0], (acc[j][i][1] * ia) * ib[1]};
             f32x2 v23 = {(acc[j][i][2] * ia) * ib[2], (acc[j][i][3] * ia) * ib[3]};
-            acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};  // cleared for the next tile
             const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
             const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
             // byte column (j*16 + nq)*2: chunk 2j + nq/8, 8 bytes in at
@@ -901,7 +912,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     }
 #endif
     // rowwise: the next tile's scales (arrived: this tile's waits counted
-    // them, or with K = 0 the one here) become reciprocals, and the scales
+    // them) become reciprocals, and the scales
     // of the tile after next go into the table this tile is done with,
     // after the stores (the next tile's first wait lets both run on).  In
     // the k-loop (hidden between matrix instructions) the conversion made
@@ -910,7 +921,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     // next tile's operands were made visible by the barrier of this tile's
     // last k-tile: no barrier here.
     if (RW) {
-      if (nk == 0) wait_vmcnt0();
       v4f *rn = FP8P_RCP_AT((tile + 1) & 1);
       *rn = recip4(*rn);
       FP8P_SCALES(b_ok, b_pi, b_m0, b_n0, tile & 1);
@@ -921,6 +931,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 #undef FP8P_H1
 #undef FP8P_E
 #undef FP8P_M
+#undef FP8P_MX
+#undef FP8P_MFZ
 #undef FP8P_MF
 #undef FP8P_RD
 #undef FP8P_SCALES
@@ -935,8 +947,34 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 
 namespace {
 
+// K = 0: the product over an empty contraction is zero.  Such problems are
+// not given to the GEMM kernel (each of its tiles has at least one k-tile,
+// which lets every tile start its accumulators from a zero input instead of
+// clearing them); this kernel writes their outputs instead: zeros, or with
+// ACC the bf16 sum of C and a zero product, fl32(C) + 0 rounded (which
+// turns -0 into +0 and keeps everything else).  n16: 16-byte chunks of C.
+template <bool F32, bool ACC>
+__global__ __launch_bounds__(256) void k_gemm_k0(void *C, int n16) {
+  v4u *c = reinterpret_cast<v4u *>(C);
+  for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < n16; i += (int)(gridDim.x * 256)) {
+    v4u v = {0u, 0u, 0u, 0u};
+    if (ACC) {
+      v = c[i];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t x = v[d];
+        const float lo = __uint_as_float(x << 16) + 0.f;
+        const float hi = __uint_as_float(x & 0xFFFF0000u) + 0.f;
+        v[d] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+      }
+    }
+    c[i] = v;
+  }
+}
+
 // One launch over the problems of d (count <= MAX_GROUP, bf16 or fp32
-// outputs per F32, accumulating per ACC); empty problems get no workgroups.
+// outputs per F32, accumulating per ACC); empty problems get no workgroups,
+// and problems with K = 0 a launch of k_gemm_k0 each.
 template <bool F32, int FA, bool ACC = false>
 hipError_t launch_group(const GemmDesc *d, int count, int rowwise, hipStream_t stream) {
   GemmGroup g = {};
@@ -945,8 +983,19 @@ hipError_t launch_group(const GemmDesc *d, int count, int rowwise, hipStream_t s
   // the problems in launch order: longest K first (stable), so that a
   // balanced schedule places the long tiles first
   int order[MAX_GROUP], n_order = 0;
-  for (int i = 0; i < count; ++i)
-    if (d[i].M != 0 && d[i].N != 0) order[n_order++] = i;
+  for (int i = 0; i < count; ++i) {
+    if (d[i].M == 0 || d[i].N == 0) continue;
+    if (d[i].K == 0) {
+      const int n16 = (int)(d[i].M * d[i].N * (F32 ? 4 : 2) / 16);
+      const int nb = n16 < 256 * 1024 ? (n16 + 255) / 256 : 1024;
+      hipLaunchKernelGGL((k_gemm_k0<F32, ACC>), dim3((unsigned)nb), dim3(256), 0, stream,
+                         d[i].C, n16);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    order[n_order++] = i;
+  }
   for (int a = 1; a < n_order; ++a)
     for (int b = a; b > 0 && d[order[b]].K > d[order[b - 1]].K; --b) {
       const int t = order[b];

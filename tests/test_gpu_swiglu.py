@@ -254,6 +254,25 @@ def test_bwd_x_acc(mnk, rowwise, e5m2):
                 "acc %s" % (mnk,))
 
 
+@pytest.mark.parametrize("rowwise", [False, True], ids=RW_IDS)
+def test_bwd_x_acc_empty_contraction(rowwise):
+    """N = 0: the product over an empty contraction is zero, so grad_x
+    becomes the bf16 sum of itself and a zero product (the oracle's bf16
+    addition): unchanged, except that -0 turns into +0."""
+    M, N, K = 64, 0, 48
+    c = W.random_bf16(67, (M, K), 1e-3, 2)
+    c.reshape(-1)[::7] = 0x8000                     # some -0 entries
+    G.say("bwd_x_acc empty contraction", (M, N, K), "rowwise", rowwise)
+    qdy = ops.fp8_linear_quantize(G.dev_bf16(np.zeros((M, N), np.uint16)), rowwise)
+    qw = ops.fp8_linear_quantize(G.dev_bf16(np.zeros((N, K), np.uint16)), rowwise)
+    gx = G.dev_bf16(c)
+    ops.fp8_linear_bwd_x_acc(qdy.q, qdy.scale, qw.qt, qw.scale_t, M, N, K, gx, rowwise)
+    torch.cuda.synchronize()
+    want = oracle.add_bf16(np.zeros((M, K), np.uint16), c)
+    assert np.array_equal(G.host(gx), want)
+    assert not np.array_equal(want, c)              # the -0 entries did change
+
+
 # ------------------------------------------------------------ whole block --
 
 def _oracle_block(x, w1, w3, w2, dy, rowwise, e5m2):
