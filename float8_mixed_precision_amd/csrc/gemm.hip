@@ -264,7 +264,11 @@ __device__ __forceinline__ v4f recip4(v4f s) {
 // 4 scales lane l of wave (wm, wn) turns into reciprocals: lanes 0-31 the
 // wave's 128 rows, lanes 32-63 its 128 columns.
 __device__ __forceinline__ int rcp_slot(int l, int wm, int wn) {
-  return l + (l < 32 ? wm * (WM / 4) : (BM + wn * WN) / 4 - 32);
+  // (l >> 5) selects the column part without a select between two
+  // wave-uniform values, which the compiler held (and spilled) in vector
+  // registers
+  const int row0 = wm * (WM / 4), col0 = (BM + wn * WN) / 4 - 32;
+  return l + row0 + (l >> 5) * (col0 - row0);
 }
 
 // Tile i (i = 0, 1, ...) of persistent workgroup b.  Workgroups are dealt
@@ -540,15 +544,16 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
   FP8P_MX(MF, 31, 4) FP8P_DMA1(DST, 15); FP8P_E()
 
 // last k-tile of a tile: the DMAs only (the next tile's first fragments are
-// read after the epilogue, which keeps them out of its registers)
-#define FP8P_H2D(DST, MF) \
+// read after the epilogue, which keeps them out of its registers), and two
+// hooks for vector work issued between its matrix instructions
+#define FP8P_H2D(DST, MF, HK1, HK2) \
   FP8P_MX(MF, 0, 4) FP8P_E() FP8P_MX(MF, 1, 4) FP8P_DMA1(DST, 0); FP8P_E() \
   FP8P_MX(MF, 2, 4) FP8P_E() FP8P_MX(MF, 3, 4) FP8P_DMA1(DST, 1); FP8P_E() \
-  FP8P_MX(MF, 4, 4) FP8P_E() FP8P_MX(MF, 5, 4) FP8P_DMA1(DST, 2); FP8P_E() \
+  FP8P_MX(MF, 4, 4) HK1; FP8P_E() FP8P_MX(MF, 5, 4) FP8P_DMA1(DST, 2); FP8P_E() \
   FP8P_MX(MF, 6, 4) FP8P_E() FP8P_MX(MF, 7, 4) FP8P_DMA1(DST, 3); FP8P_E() \
   FP8P_MX(MF, 8, 4) FP8P_E() FP8P_MX(MF, 9, 4) FP8P_DMA1(DST, 4); FP8P_E() \
   FP8P_MX(MF, 10, 4) FP8P_E() FP8P_MX(MF, 11, 4) FP8P_DMA1(DST, 5); FP8P_E() \
-  FP8P_MX(MF, 12, 4) FP8P_E() FP8P_MX(MF, 13, 4) FP8P_DMA1(DST, 6); FP8P_E() \
+  FP8P_MX(MF, 12, 4) HK2; FP8P_E() FP8P_MX(MF, 13, 4) FP8P_DMA1(DST, 6); FP8P_E() \
   FP8P_MX(MF, 14, 4) FP8P_E() FP8P_MX(MF, 15, 4) FP8P_DMA1(DST, 7); FP8P_E() \
   FP8P_MX(MF, 16, 4) FP8P_E() FP8P_MX(MF, 17, 4) FP8P_DMA1(DST, 8); FP8P_E() \
   FP8P_MX(MF, 18, 4) FP8P_E() FP8P_MX(MF, 19, 4) FP8P_DMA1(DST, 9); FP8P_E() \
@@ -639,9 +644,10 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
     }
     // the last k-tile (MF: FP8P_MF, or FP8P_MFZ when it is also the first).
     // It waits for everything but, where it follows the previous epilogue
-    // directly (K <= 128, bf16 tensorwise), that epilogue's stores (rowwise:
-    // the next tile's scales, issued after them, must have arrived by the
-    // end of this epilogue).
+    // directly (K <= 128, bf16 tensorwise), that epilogue's stores.
+    // Rowwise, the next tile's scales (issued after those stores, so this
+    // wait counts them) become reciprocals between its matrix
+    // instructions.
 #define FP8P_LAST(MF)                                                             \
   do {                                                                            \
     FP8P_H1(st, MF)                                                               \
@@ -651,7 +657,13 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       wait_vmcnt0();                                                              \
     wait_lgkm0();                                                                 \
     barrier_lds();                                                                \
-    FP8P_H2D(st, MF)                                                              \
+    v4f *rn_ = nullptr;                                                           \
+    v4f sn_ = {};                                                                 \
+    if (RW) {                                                                     \
+      rn_ = FP8P_RCP_AT((tile + 1) & 1);                                          \
+      sn_ = *rn_;                                                                 \
+    }                                                                             \
+    FP8P_H2D(st, MF, if (RW) sn_ = recip4(sn_), if (RW) *rn_ = sn_)               \
     FP8P_DADV();                                                                  \
     st ^= 1;                                                                      \
   } while (0)
@@ -911,20 +923,12 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       d[4] = ph_t1; d[5] = ph_r1; d[6] = ph_t2; d[7] = ph_r2;
     }
 #endif
-    // rowwise: the next tile's scales (arrived: this tile's waits counted
-    // them) become reciprocals, and the scales
-    // of the tile after next go into the table this tile is done with,
-    // after the stores (the next tile's first wait lets both run on).  In
-    // the k-loop (hidden between matrix instructions) the conversion made
-    // the compiler clear the accumulators twice per tile.  A wave stages and
-    // keeps its scales only in its own part of the epilogue region, and the
-    // next tile's operands were made visible by the barrier of this tile's
-    // last k-tile: no barrier here.
-    if (RW) {
-      v4f *rn = FP8P_RCP_AT((tile + 1) & 1);
-      *rn = recip4(*rn);
-      FP8P_SCALES(b_ok, b_pi, b_m0, b_n0, tile & 1);
-    }
+    // rowwise: the scales of the tile after next go into the table this
+    // tile is done with, after the stores (the next tile's first wait lets
+    // both run on).  A wave stages and keeps its scales only in its own part
+    // of the epilogue region, and the next tile's operands were made visible
+    // by the barrier of this tile's last k-tile: no barrier here.
+    if (RW) FP8P_SCALES(b_ok, b_pi, b_m0, b_n0, tile & 1);
   }
 #undef FP8P_H2D
 #undef FP8P_H2
