@@ -211,7 +211,8 @@ __device__ __forceinline__ T pick(const T (&v)[MAX_GROUP], int i) {
 // of 32 rows per wave, 16-byte chunks XOR-swizzled by row instead of
 // padding), so it never touches the operand stages that are filling for the
 // next tile; it leaves its stores in flight while the next tile's first
-// k-tile starts, and clears each accumulator block once it is stored.
+// k-tile starts.  No tile clears its accumulators: the MFMAs of each tile's
+// first k-tile take a zero accumulator input.
 // Nothing is shared between workgroups: correctness does not depend on how
 // many are resident at once.
 constexpr int EPI_OFF = 2 * STAGE_BYTES;        // 128 KB
@@ -224,7 +225,8 @@ constexpr int EPI_STORES = 32;
 // staging (tiles of even and odd index) and stages its rowwise epilogues in
 // the second half.  A tile's scales are transferred two tiles ahead, after
 // the stores of an epilogue (SCALE_DMAS transfers, always issued), and
-// become reciprocals at the end of the epilogue before it.
+// become reciprocals between the MFMAs of the last k-tile of the tile
+// before it.
 constexpr int SCALE_DMAS = 2;
 constexpr int RW_STAGE_OFF = EPI_WAVE_BYTES / 2;
 static_assert(2 * SCALE_BYTES <= RW_STAGE_OFF, "two scale tables below the rowwise staging");
