@@ -149,6 +149,20 @@ def test_bwd_w_f32(mnk, rowwise):
 
 
 @pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
+def test_bwd_w_f32_empty_contraction(rowwise):
+    """M = 0 tokens: grad_W is the product over an empty contraction, all
+    zeros (fp32 +0), whatever the output held before."""
+    M, N, K = 0, 48, 80
+    G.say("bwd_w_f32 empty contraction", (M, N, K), "rowwise", rowwise)
+    qx = ops.fp8_linear_quantize(G.dev_bf16(np.zeros((M, K), np.uint16)), rowwise)
+    qdy = ops.fp8_linear_quantize(G.dev_bf16(np.zeros((M, N), np.uint16)), rowwise)
+    g32 = torch.full((N, K), -3.5, dtype=torch.float32, device=G.DEV)
+    ops.fp8_linear_bwd_w_f32(qdy.qt, qdy.scale_t, qx.qt, qx.scale_t, M, N, K, rowwise, g32)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.host(g32).view(np.uint32), np.zeros((N, K), np.uint32))
+
+
+@pytest.mark.parametrize("rowwise", [False, True], ids=["tensorwise", "rowwise"])
 def test_bwd_w_f32_full_size(rowwise):
     """The Llama-3.1-8B FFN w1 grad_W (N 14336, K 4096, contraction 8192),
     sampled against the oracle."""
