@@ -490,7 +490,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
       fb[J], fa[I], (v4f){0.f, 0.f, 0.f, 0.f}, 0, FA, 0, 0, 0, 0)
 // step S of a half k-tile with MF (FP8P_MF or FP8P_MFZ)
 #define FP8P_MX(MF, S, I0) MF((S) / 4, (I0) + ((((S) / 4) & 1) ? (S) % 4 : 3 - (S) % 4));
-#define FP8P_M(S, I0) FP8P_MX(FP8P_MF, S, I0)
 #define FP8P_E() __builtin_amdgcn_sched_barrier(0);
 #define FP8P_H1(ST, MF) \
   FP8P_MX(MF, 0, 0) FP8P_RD(ST, 0, 7, 0); FP8P_E() \
@@ -936,7 +935,6 @@ __global__ __launch_bounds__(THREADS) void k_gemm_fp8_pers(GemmGroup g) {
 #undef FP8P_H2
 #undef FP8P_H1
 #undef FP8P_E
-#undef FP8P_M
 #undef FP8P_MX
 #undef FP8P_MFZ
 #undef FP8P_MF
