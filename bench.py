@@ -44,8 +44,9 @@ def parse():
     p.add_argument("--workload", default="ffn8b_tw")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timing (e.g. under a profiler)")
-    p.add_argument("--cpu-rows", type=int, default=128,
-                   help="output rows per GEMM in the CPU oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=512,
+                   help="output rows per GEMM in the CPU oracle sample (four times "
+                        "as many rows of every quantize input)")
     p.add_argument("--no-next-rows", action="store_true",
                    help="skip the next_rows measurements (profiling runs of the step alone)")
     p.add_argument("--ffn-block-only", action="store_true",
@@ -927,7 +928,7 @@ def main():
         result["parity"] = step_parity(samples)
         del samples
         print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows, 4 * args.cpu_rows)
     print(json.dumps(result), flush=True)
 
 
