@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--workload", default="ffn8b_tw")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timing (e.g. under a profiler)")
-    p.add_argument("--cpu-rows", type=int, default=512,
+    p.add_argument("--cpu-rows", type=int, default=640,
                    help="output rows per GEMM in the CPU oracle sample (four times "
                         "as many rows of every quantize input)")
     p.add_argument("--no-next-rows", action="store_true",
