@@ -33,16 +33,20 @@ namespace {
 constexpr int TW_UNROLL = 8;
 constexpr int TW_CHUNK = AM_THREADS * TW_UNROLL;   // 16-byte vectors per chunk
 
-// cast tile: 128 rows x 128 columns per 256-thread workgroup.
+// cast tile: 128 rows x 128 columns per 512-thread workgroup, one 4-row
+// group per thread (a single pass: no thread's loads wait behind its own
+// earlier stores, which complete in issue order).
 constexpr int CT_T = 128;
-constexpr int CT_THREADS = 256;
+constexpr int CT_THREADS = 512;
+constexpr int CT_PASSES = CT_T / (CT_THREADS / 16 * 4);
+static_assert(CT_PASSES >= 1 && CT_T % (CT_THREADS / 16 * 4) == 0, "cast rows per pass");
 // Tile order of the cast: groups of CT_GROUP row tiles, the row tile
 // fastest within a group, so the workgroups running at one time write
 // neighbouring 128-byte segments of each qt row.  q and qt are written with
 // non-temporal stores when CT_NT.  (Both are set from measurements of the
 // whole step; see the notes at k_cast_transpose.)
 #ifndef FP8L_CAST_GROUP
-#define FP8L_CAST_GROUP 4
+#define FP8L_CAST_GROUP 2
 #endif
 #ifndef FP8L_CAST_NT
 #define FP8L_CAST_NT 0
@@ -93,26 +97,27 @@ __global__ __launch_bounds__(AM_THREADS) void k_amax_tw(
 // The tensor's amax from the nb partial maxima, by a whole 256-thread block
 // (all loads in flight together, index clamped and value masked); nb = 0 is
 // an empty tensor: amax 0.  Returns the u16 bits of |amax| to every thread.
+template <int NTHR>
 __device__ __forceinline__ uint32_t tw_amax_bits(const uint32_t *__restrict__ part, int nb,
                                                  uint32_t *red) {
   const int tid = threadIdx.x;
   uint32_t t = 0;
   if (nb > 0) {
-    uint32_t pv[TW_MAX_BLOCKS / AM_THREADS];
+    uint32_t pv[TW_MAX_BLOCKS / NTHR];
 #pragma unroll
-    for (int k = 0; k < TW_MAX_BLOCKS / AM_THREADS; ++k) {
-      const int i = tid + k * AM_THREADS;
+    for (int k = 0; k < TW_MAX_BLOCKS / NTHR; ++k) {
+      const int i = tid + k * NTHR;
       pv[k] = part[i < nb ? i : nb - 1];
     }
 #pragma unroll
-    for (int k = 0; k < TW_MAX_BLOCKS / AM_THREADS; ++k) t = max(t, pv[k]);
+    for (int k = 0; k < TW_MAX_BLOCKS / NTHR; ++k) t = max(t, pv[k]);
   }
   t = wave_max(t);
   if ((tid & 63) == 0) red[tid >> 6] = t;
   __syncthreads();
   uint32_t mm = red[0];
 #pragma unroll
-  for (int w = 1; w < AM_THREADS / 64; ++w) mm = max(mm, red[w]);
+  for (int w = 1; w < NTHR / 64; ++w) mm = max(mm, red[w]);
   return mm;
 }
 
@@ -120,7 +125,7 @@ __device__ __forceinline__ uint32_t tw_amax_bits(const uint32_t *__restrict__ pa
 __global__ __launch_bounds__(AM_THREADS) void k_amax_finish(
     const uint32_t *__restrict__ part, int nb, float *amax_out) {
   __shared__ uint32_t red[AM_THREADS / 64];
-  const uint32_t am = tw_amax_bits(part, nb, red);
+  const uint32_t am = tw_amax_bits<AM_THREADS>(part, nb, red);
   if (threadIdx.x == 0) amax_out[0] = bf16_to_f32(am);
 }
 
@@ -251,8 +256,8 @@ __global__ __launch_bounds__(256) void k_finalize_rowwise(
 // -------------------------------------------------------- cast+transpose --
 //
 // Tile of 128 rows x 128 columns.  Thread (c8, rg): c8 = tid % 16 selects an
-// 8-column chunk, rg = tid / 16 a group of 4 consecutive rows; two passes
-// cover rows rg*4 + {0..3} and 64 + rg*4 + {0..3}.
+// 8-column chunk, rg = tid / 16 a group of 4 consecutive rows, rows
+// rg*4 + {0..3} (one pass with 512 threads).
 //
 // Phase A: 16-byte coalesced loads of bf16 (a wave reads 4 rows x 256 B per
 // instruction), scale, convert, 8-byte stores of q (4 rows x 128 B per
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
     s_t = scale[0];
   } else {
     __shared__ uint32_t red[CT_THREADS / 64];
-    const uint32_t am = tw_amax_bits(part, nparts, red);
+    const uint32_t am = tw_amax_bits<CT_THREADS>(part, nparts, red);
     const float a = bf16_to_f32(am);
     s_t = scale_from_amax<FMT>(a);
     if (blockIdx.x == 0 && tid == 0) {
@@ -328,8 +333,8 @@ __global__ __launch_bounds__(CT_THREADS) void k_cast_transpose(
   }
 
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int rl = pass * 64 + rg * 4;   // local row of the 4-row group
+  for (int pass = 0; pass < CT_PASSES; ++pass) {
+    const int rl = pass * (CT_THREADS / 4) + rg * 4;   // local row of the 4-row group
     const int r = r0 + rl;
     // rows is a multiple of 16, so the 4 rows are all in or all out
     const bool ok = col_ok && r < rows;
