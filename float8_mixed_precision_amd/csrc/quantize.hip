@@ -94,7 +94,7 @@ __global__ __launch_bounds__(AM_THREADS) void k_amax_tw(
   }
 }
 
-// The tensor's amax from the nb partial maxima, by a whole 256-thread block
+// The tensor's amax from the nb partial maxima, by a whole NTHR-thread block
 // (all loads in flight together, index clamped and value masked); nb = 0 is
 // an empty tensor: amax 0.  Returns the u16 bits of |amax| to every thread.
 template <int NTHR>
