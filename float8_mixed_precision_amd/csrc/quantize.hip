@@ -100,6 +100,7 @@ __global__ __launch_bounds__(AM_THREADS) void k_amax_tw(
 template <int NTHR>
 __device__ __forceinline__ uint32_t tw_amax_bits(const uint32_t *__restrict__ part, int nb,
                                                  uint32_t *red) {
+  static_assert(TW_MAX_BLOCKS % NTHR == 0 && NTHR % 64 == 0, "whole waves, equal shares");
   const int tid = threadIdx.x;
   uint32_t t = 0;
   if (nb > 0) {
